@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark for libpagedattn on one MI355X.
+
+A step is one paged_attn_decode call over the whole batch (phase 1 with the
+tier dispatch, then phase 2).  The default workload is long-context decode:
+4 sequences x 102400 tokens (200 partitions of 512), 24 query / 4 KV heads,
+head_dim 256, 16-token pages, fp16, q = 8 N(0,1) so the softmax is peaked.
+
+Prints one JSON line.  `value` is the effective KV-cache read bandwidth of the
+whole step (sum of seq_len x KV heads x head_dim x 2 bytes x 2 (K and V),
+divided by the step time), with every input already resident in HBM.
+`roofline` is the phase-1 kernel (the dominant one) timed with HIP events on
+the launch stream.  `cpu_baseline` is the fp64 CPU oracle timed on this host.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "pa_phase1_kernel_long-4x102400_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "gqa_aware_paged_amd", "csrc", f)
+                  for f in ("pa_kernels.h", "pagedattn.hip")]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        ev = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        assert self.hip.hipEventSynchronize(ctypes.c_void_p(b)) == 0
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a),
+                                            ctypes.c_void_p(b)) == 0
+        return ms.value
+
+    def destroy(self, ev: int):
+        self.hip.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def traffic_from_counters(units_bytes):
+    """HBM bytes per phase-1 launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on different kernel sources."""
+    if not os.path.exists(COUNTERS):
+        return None
+    c = json.load(open(COUNTERS))
+    if c.get("kernel_sources_sha256_16") != kernel_hash():
+        return None
+    fetch = c["FETCH_SIZE_KiB_per_dispatch"] * 1024 * c["fetch_scale"]
+    write = c["WRITE_SIZE_KiB_per_dispatch"] * 1024 * c["write_scale"]
+    return fetch + write
+
+
+def cpu_baseline(w, nseqs: int):
+    """Time the fp64 oracle (as it stands) on the first `nseqs` sequences, all heads."""
+    import oracle
+    seqs = list(range(min(nseqs, w.num_seqs)))
+    kp, vp, bt, sl = w.host_pages(seqs)
+    q = w.q[seqs].cpu()
+    t0 = time.perf_counter()
+    _, threads = oracle.decode(q, kp, vp, bt, sl, w.scale, w.dtype, return_threads=True)
+    dt = time.perf_counter() - t0
+    kvb = int(sl.astype("int64").sum()) * w.num_kv_heads * w.head_dim * 2 * 2
+    full = w.kv_bytes / kvb
+    return {"value": kvb / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(seqs)} of {w.num_seqs} sequences, all {w.num_heads} query heads, "
+                      f"fp64 C oracle with OpenMP ({dt:.2f} s)",
+            "seconds": dt, "us_per_step_extrapolated": dt * full * 1e6}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long",
+                    choices=["tiny", "batch", "long", "mixed", "saturation"])
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--single-pass-max-len", type=int, default=None)
+    ap.add_argument("--cpu-seqs", type=int, default=4,
+                    help="sequences of the workload the CPU oracle is timed on")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one device copy of this size first (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the decode path runs on a single MI355X and has no "
+              "multi-GPU mode; use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gqa_aware_paged_amd as pa
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pa.lib()
+
+    log(f"generating workload {args.workload}")
+    kw = {}
+    if args.partition_size is not None and args.workload == "mixed":
+        kw["partition_size"] = args.partition_size
+    w = workloads.NAMED[args.workload](device="cuda", **kw)
+    P = args.partition_size if args.partition_size is not None else w.partition_size
+    torch.cuda.synchronize()
+
+    dec = pa.Decoder(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                     w.max_blocks_per_seq, w.q.dtype, max_seq_len=w.max_seq_len,
+                     partition_size=P, single_pass_max_len=args.single_pass_max_len)
+    info = pa.plan(list(w.seq_lens_host), w.num_heads, w.num_kv_heads, w.head_dim,
+                   w.block_size, w.max_blocks_per_seq, w.max_seq_len, P,
+                   single_pass_max_len=args.single_pass_max_len)
+    log(f"plan: {info}")
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {n} bytes read, {n} bytes written")
+        del src, dst
+
+    ev = HipEvents()
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        dec(w.q, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, w.scale)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        dec(w.q, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, w.scale,
+            events=pairs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = start.elapsed_time(stop) / args.steps
+    ph1 = sorted(ev.elapsed_ms(a, b) for a, b in pairs)
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    ph1_avg = sum(ph1) / len(ph1)
+    log(f"timed {args.steps} steps: {step_ms * 1e3:.1f} us/step (wall {wall:.3f} s), "
+        f"phase-1 avg {ph1_avg * 1e3:.1f} us, median {ph1[len(ph1) // 2] * 1e3:.1f} us")
+
+    # algorithmic bytes: one unit = one (token, KV head); it reads a K row and a V row
+    units = int(w.seq_lens_host.clip(0).astype("int64").sum()) * w.num_kv_heads
+    bytes_per_unit = 2 * w.head_dim * 2
+    kv = units * bytes_per_unit
+    assert kv == w.kv_bytes
+    eff = kv / (step_ms * 1e-3) / 1e9
+    achieved = kv / (ph1_avg * 1e-3) / 1e9
+    rec = {
+        "metric": "decode attention us/step + effective KV-cache GB/s (% of HBM peak), 1 GPU",
+        "value": round(eff, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "us_per_step": round(step_ms * 1e3, 2),
+        "pct_hbm_peak": round(100 * eff / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs,
+                   "seq_lens": "all 102400" if args.workload == "long" else
+                   f"{int(w.seq_lens_host.min())}..{int(w.seq_lens_host.max())}",
+                   "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "block_size": w.block_size, "partition_size": P,
+                   "single_pass_max_len": info["single_pass_max_len"],
+                   "kv_bytes_per_step": kv, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "pa_phase1_kernel",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_counters(kv) if args.workload == "long" else None,
+                     "algorithmic_bytes_per_launch": kv, "bytes_per_unit": bytes_per_unit,
+                     "units_per_launch": units,
+                     "avg_launch_us": round(ph1_avg * 1e3, 2)},
+    }
+    if not args.no_cpu:
+        log(f"timing the CPU oracle on {min(args.cpu_seqs, w.num_seqs)} sequences")
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seqs)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

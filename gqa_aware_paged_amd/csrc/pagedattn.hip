@@ -1,0 +1,282 @@
+// Host side of libpagedattn: argument validation, the length-tiered plan, and the
+// launches of the gfx950 kernels in pa_kernels.h.  C ABI in include/pagedattn.h.
+//
+// Tiering follows the three-tier decode dispatch on the page of commit b80fd2b
+// (short sequences in one workgroup, long ones split into partitions merged in
+// a second kernel), re-thresholded for 256 compute units: one pass only pays
+// when the batch alone supplies enough workgroups; otherwise every sequence
+// longer than one partition is split.  The partition size is an argument, as
+// the page of commit 8d26e23 asks ("should be tunable"); 0 selects 512.
+#include "pagedattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "pa_kernels.h"
+
+#define PA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kWaves = 4;                   // waves per phase-1 workgroup
+constexpr int kDefaultPartition = 512;      // tokens
+constexpr int kDefaultCUs = 256;            // MI355X
+constexpr int kPagesSinglePassMax = 8192;   // one-pass bound when the batch fills the GPU
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct Plan {
+  int P = 0;             // partition size (tokens)
+  int T1 = 0;            // single-pass threshold (tokens)
+  int max_parts = 0;     // partitions per (seq, kv head) slot; 0 = no phase 2
+  int max_seq_len = 0;   // resolved length bound
+  int group = 0;
+  long long grid1 = 0, grid2 = 0;
+  size_t ws_acc_bytes = 0, ws_bytes = 0;
+};
+
+bool supported_head_dim(int d) { return d == 128 || d == 256; }
+
+// Validation shared by every entry point (pointers excepted).
+int check_sizes(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int P, int dtype) {
+  if (S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || mbps < 0) return PA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return PA_ERR_SHAPE;
+  if (P < 0 || P % 16 != 0) return PA_ERR_PARTITION;
+  if (dtype != PA_F16 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (!supported_head_dim(D)) return PA_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 16) return PA_ERR_UNSUPPORTED;
+  if (bs % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (S > 0 && mbps < 1) return PA_ERR_SHAPE;
+  const long long cap = static_cast<long long>(mbps) * bs;
+  if (max_len > cap) return PA_ERR_SHAPE;
+  if (cap > std::numeric_limits<int>::max()) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int P_req,
+              const pa_options* opt, Plan& pl) {
+  pl = Plan{};
+  pl.group = Hq / Hkv;
+  pl.P = P_req > 0 ? P_req : kDefaultPartition;
+  pl.max_seq_len = max_len > 0 ? max_len : mbps * bs;
+  const int cus = (opt && opt->num_cus > 0) ? opt->num_cus : kDefaultCUs;
+  if (opt && opt->single_pass_max_len >= 0) {
+    pl.T1 = opt->single_pass_max_len;
+  } else {
+    const long long slots = static_cast<long long>(S) * Hkv;
+    pl.T1 = slots >= 4LL * cus ? (kPagesSinglePassMax > pl.P ? kPagesSinglePassMax : pl.P)
+                               : pl.P;
+  }
+  if (pl.max_seq_len > pl.T1) pl.max_parts = (pl.max_seq_len + pl.P - 1) / pl.P;
+  const long long parts = pl.max_parts > 0 ? pl.max_parts : 1;
+  pl.grid1 = static_cast<long long>(S) * Hkv * parts;
+  pl.grid2 = pl.max_parts > 0 ? static_cast<long long>(S) * Hkv * (D / pa::kRedSlice) : 0;
+  if (pl.grid1 > std::numeric_limits<int>::max() || pl.grid2 > std::numeric_limits<int>::max())
+    return PA_ERR_SHAPE;
+  if (pl.max_parts > 0) {
+    const size_t recs = static_cast<size_t>(S) * Hq * pl.max_parts;
+    pl.ws_acc_bytes = (recs * D * sizeof(float) + 255) & ~static_cast<size_t>(255);
+    pl.ws_bytes = pl.ws_acc_bytes + recs * sizeof(float2);
+  }
+  return PA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+template <int D, class DT>
+int launch_decode(const pa::DecodeArgs& args, const Plan& pl, hipStream_t stream,
+                  const pa_options* opt) {
+  if (opt && opt->phase1_begin) {
+    if (hipEventRecord(opt->phase1_begin, stream) != hipSuccess) return PA_ERR_HIP;
+  }
+  hipLaunchKernelGGL((pa::pa_phase1_kernel<D, DT, kWaves>), dim3(static_cast<unsigned>(pl.grid1)),
+                     dim3(kWaves * 64), 0, stream, args);
+  if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  if (opt && opt->phase1_end) {
+    if (hipEventRecord(opt->phase1_end, stream) != hipSuccess) return PA_ERR_HIP;
+  }
+  if (pl.grid2 > 0) {
+    const size_t lds = static_cast<size_t>(pl.group) * pa::kRedGroups * pa::kRedQuads * 16;
+    hipLaunchKernelGGL((pa::pa_reduce_kernel<D, DT>), dim3(static_cast<unsigned>(pl.grid2)),
+                       dim3(pa::kRedThreads), lds, stream, args);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+PA_API const char* paged_attn_status_str(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK: success";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: inconsistent sizes";
+    case PA_ERR_UNSUPPORTED:
+      return "PA_ERR_UNSUPPORTED: head_dim must be 128 or 256, group 1..16, block_size a "
+             "multiple of 16, dtype f16 or bf16";
+    case PA_ERR_PARTITION: return "PA_ERR_PARTITION: partition_size must be 0 or a multiple of 16";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: a HIP launch failed";
+    case PA_ERR_ALIGN: return "PA_ERR_ALIGN: pointer alignment (16 B for q and caches, 8 B for out, 256 B for workspace)";
+    default: return "unknown pa_status_t";
+  }
+}
+
+PA_API size_t paged_attn_workspace_size_ex(int num_seqs, int num_heads, int num_kv_heads,
+                                           int head_dim, int block_size, int max_blocks_per_seq,
+                                           int max_seq_len, int partition_size,
+                                           const pa_options* opt) {
+  if (check_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                  max_seq_len, partition_size, PA_F16) != PA_OK)
+    return static_cast<size_t>(-1);
+  Plan pl;
+  if (make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                max_seq_len, partition_size, opt, pl) != PA_OK)
+    return static_cast<size_t>(-1);
+  return pl.ws_bytes;
+}
+
+PA_API size_t paged_attn_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
+                                        int head_dim, int block_size, int max_blocks_per_seq,
+                                        int max_seq_len, int partition_size) {
+  return paged_attn_workspace_size_ex(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                      max_blocks_per_seq, max_seq_len, partition_size, nullptr);
+}
+
+PA_API int paged_attn_plan(const int32_t* seq_lens_host, int num_seqs, int num_heads,
+                           int num_kv_heads, int head_dim, int block_size,
+                           int max_blocks_per_seq, int max_seq_len, int partition_size,
+                           int dtype, const pa_options* opt, pa_plan_info* info) {
+  if (!info) return PA_ERR_NULL;
+  int st = check_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       max_blocks_per_seq, max_seq_len, partition_size, dtype);
+  if (st != PA_OK) return st;
+  Plan pl;
+  st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                 max_seq_len, partition_size, opt, pl);
+  if (st != PA_OK) return st;
+  *info = pa_plan_info{};
+  info->partition_size = pl.P;
+  info->single_pass_max_len = pl.T1;
+  info->max_partitions = pl.max_parts;
+  info->group = pl.group;
+  info->phase1_workgroups = pl.grid1;
+  info->phase2_workgroups = pl.grid2;
+  info->workspace_bytes = pl.ws_bytes;
+  info->threads_per_workgroup = kWaves * 64;
+  info->lds_bytes_phase1 = kWaves * 2 * pa::kTile * head_dim * 2;
+  if (seq_lens_host) {
+    for (int s = 0; s < num_seqs; ++s) {
+      int L = seq_lens_host[s] < pl.max_seq_len ? seq_lens_host[s] : pl.max_seq_len;
+      if (L <= pl.T1) {
+        info->single_pass_seqs++;
+        info->active_workgroups += num_kv_heads;
+      } else {
+        info->partitioned_seqs++;
+        info->active_workgroups += static_cast<long long>(num_kv_heads) *
+                                   ((L + pl.P - 1) / pl.P);
+      }
+    }
+  }
+  return PA_OK;
+}
+
+PA_API int paged_attn_decode_ex(void* out, const void* q, const void* key_cache,
+                                const void* value_cache, const int32_t* block_tables,
+                                const int32_t* seq_lens, int num_seqs, int num_heads,
+                                int num_kv_heads, int head_dim, int block_size, float scale,
+                                int partition_size, void* workspace, hipStream_t stream,
+                                int max_blocks_per_seq, int max_seq_len, int dtype,
+                                size_t workspace_bytes, const pa_options* opt) {
+  int st = check_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       max_blocks_per_seq, max_seq_len, partition_size, dtype);
+  if (st != PA_OK) return st;
+  if (!std::isfinite(scale)) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !key_cache || !value_cache || !block_tables || !seq_lens) return PA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
+      !aligned(out, 8) || !aligned(block_tables, 4) || !aligned(seq_lens, 4))
+    return PA_ERR_ALIGN;
+  Plan pl;
+  st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                 max_seq_len, partition_size, opt, pl);
+  if (st != PA_OK) return st;
+  if (pl.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < pl.ws_bytes) return PA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return PA_ERR_ALIGN;
+  }
+
+  pa::DecodeArgs args{};
+  args.out = out;
+  args.q = static_cast<const uint16_t*>(q);
+  args.kc = static_cast<const uint16_t*>(key_cache);
+  args.vc = static_cast<const uint16_t*>(value_cache);
+  args.bt = block_tables;
+  args.seq_lens = seq_lens;
+  args.ws_acc = pl.ws_bytes ? static_cast<float*>(workspace) : nullptr;
+  args.ws_ml = pl.ws_bytes ? reinterpret_cast<float2*>(static_cast<char*>(workspace) +
+                                                       pl.ws_acc_bytes)
+                           : nullptr;
+  args.num_seqs = num_seqs;
+  args.num_heads = num_heads;
+  args.num_kv_heads = num_kv_heads;
+  args.group = pl.group;
+  args.block_size = block_size;
+  args.max_blocks_per_seq = max_blocks_per_seq;
+  args.max_seq_len = pl.max_seq_len;
+  args.partition_size = pl.P;
+  args.single_pass_max_len = pl.T1;
+  args.max_parts = pl.max_parts;
+  args.scale_log2 = scale * kLog2e;
+
+  if (head_dim == 256)
+    return dtype == PA_F16 ? launch_decode<256, pa::F16>(args, pl, stream, opt)
+                           : launch_decode<256, pa::BF16>(args, pl, stream, opt);
+  return dtype == PA_F16 ? launch_decode<128, pa::F16>(args, pl, stream, opt)
+                         : launch_decode<128, pa::BF16>(args, pl, stream, opt);
+}
+
+PA_API int paged_attn_decode(void* out, const void* q, const void* key_cache,
+                             const void* value_cache, const int32_t* block_tables,
+                             const int32_t* seq_lens, int num_seqs, int num_heads,
+                             int num_kv_heads, int head_dim, int block_size, float scale,
+                             int partition_size, void* workspace, hipStream_t stream,
+                             int max_blocks_per_seq, int max_seq_len, int dtype,
+                             size_t workspace_bytes) {
+  return paged_attn_decode_ex(out, q, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                              num_heads, num_kv_heads, head_dim, block_size, scale,
+                              partition_size, workspace, stream, max_blocks_per_seq,
+                              max_seq_len, dtype, workspace_bytes, nullptr);
+}
+
+PA_API int paged_attn_gather_probe(void* k_out, void* v_out, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   const int32_t* seq_lens, int num_seqs, int num_kv_heads,
+                                   int head_dim, int block_size, int max_blocks_per_seq,
+                                   int max_seq_len, hipStream_t stream) {
+  int st = check_sizes(num_seqs, num_kv_heads, num_kv_heads, head_dim, block_size,
+                       max_blocks_per_seq, max_seq_len, 0, PA_F16);
+  if (st != PA_OK) return st;
+  if (max_seq_len <= 0) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!k_out || !v_out || !key_cache || !value_cache || !block_tables || !seq_lens)
+    return PA_ERR_NULL;
+  if (!aligned(k_out, 16) || !aligned(v_out, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16))
+    return PA_ERR_ALIGN;
+  const long long grid = static_cast<long long>(num_seqs) * num_kv_heads;
+  if (grid > std::numeric_limits<int>::max()) return PA_ERR_SHAPE;
+  pa::GatherArgs g{static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out),
+                   static_cast<const uint16_t*>(key_cache),
+                   static_cast<const uint16_t*>(value_cache), block_tables, seq_lens,
+                   num_seqs, num_kv_heads, block_size, max_blocks_per_seq, max_seq_len};
+  if (head_dim == 256)
+    hipLaunchKernelGGL(pa::pa_gather_kernel<256>, dim3(static_cast<unsigned>(grid)), dim3(256),
+                       0, stream, g);
+  else
+    hipLaunchKernelGGL(pa::pa_gather_kernel<128>, dim3(static_cast<unsigned>(grid)), dim3(256),
+                       0, stream, g);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}

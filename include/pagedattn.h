@@ -1,0 +1,211 @@
+/*
+ * libpagedattn — GQA-grouped, partitioned paged-attention decode for MI355X (gfx950).
+ *
+ * One call computes, for every sequence s and query head h,
+ *
+ *     out[s,h,:] = sum_t softmax_t(scale * q[s,h,:] . K_t) V_t ,   t in [0, seq_lens[s])
+ *
+ * where token t is read from physical page block_tables[s][t / block_size] at
+ * slot t % block_size, and query head h reads KV head h / (num_heads / num_kv_heads).
+ *
+ * Method (pages of commits 8d26e23 "docs", b80fd2b "paged_attn.py" and
+ * 87a19d2 "paged_attention_v2_triton.py"):
+ *   - grid on KV heads, not query heads: one workgroup serves the whole group of
+ *     query heads that share a KV head, so each K/V page is read once
+ *     (8d26e23, "Key design change");
+ *   - phase 1 produces, per (sequence, KV head, partition), the compound partial
+ *     (max_score, exp_sum, weighted_v[head_dim]) for every query head of the
+ *     group (8d26e23, compound type and phase-1 kernel);
+ *   - phase 2 merges the partials with the flash-attention rescale
+ *     alpha = exp(m_i - m_new), beta = exp(m_ij - m_new) (8d26e23 phase-2 kernel;
+ *     87a19d2 online-softmax fix);
+ *   - a length-tiered dispatch runs short sequences in one pass and splits long
+ *     ones into partitions (b80fd2b, three-tier decode dispatch; 8d26e23, the
+ *     partition size should be tunable).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers unless a parameter says "host".
+ *   - The caller owns every buffer.  The library never allocates or frees device
+ *     memory, never synchronises the device or the stream, and keeps no pointer
+ *     after returning.  It has no mutable global state: concurrent calls on
+ *     different streams are safe when their `out` and `workspace` differ.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and runs asynchronously.  All host-side validation happens before the
+ *     first HIP call; a rejected call enqueues nothing.
+ *   - Errors are returned as pa_status_t.  There is no fallback path: a shape
+ *     the kernels do not support is rejected, never served another way.
+ *   - Device faults (for example a page id outside the pool, which the library
+ *     cannot see) surface at the caller's next synchronisation.
+ *
+ * Layouts (all contiguous, row-major):
+ *   q, out        [num_seqs][num_heads][head_dim]                       dtype
+ *   key_cache     [num_blocks][num_kv_heads][block_size][head_dim]      dtype
+ *   value_cache   [num_blocks][num_kv_heads][block_size][head_dim]      dtype
+ *   block_tables  [num_seqs][max_blocks_per_seq]                        int32
+ *   seq_lens      [num_seqs]                                            int32
+ *   One (page, KV head) is one contiguous block_size*head_dim chunk.
+ *   Entries of a block-table row at or past ceil(seq_lens[s]/block_size) are
+ *   never read; slots at or past seq_lens[s] in the last page are never used
+ *   (they may hold NaN).
+ *
+ * Supported shapes: head_dim 128 or 256; num_heads / num_kv_heads (the group)
+ * 1..16; block_size a multiple of 16; partition_size 0 (automatic) or a positive
+ * multiple of 16; dtype f16 or bf16 (q, caches and out share it).
+ * Pointers q, key_cache and value_cache must be 16-byte aligned, out 8-byte
+ * aligned and workspace 256-byte aligned (every torch allocation is).
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_dtype_t {
+    PA_F16 = 0,
+    PA_BF16 = 1
+} pa_dtype_t;
+
+typedef enum pa_status_t {
+    PA_OK = 0,
+    PA_ERR_NULL = 1,         /* a required pointer is NULL                       */
+    PA_ERR_SHAPE = 2,        /* inconsistent sizes (heads, lengths, table)       */
+    PA_ERR_UNSUPPORTED = 3,  /* valid but not built: head_dim, group, dtype, bs  */
+    PA_ERR_PARTITION = 4,    /* partition_size not 0 and not a multiple of 16    */
+    PA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required          */
+    PA_ERR_HIP = 6,          /* a kernel launch failed                           */
+    PA_ERR_ALIGN = 7         /* a pointer is not aligned as required             */
+} pa_status_t;
+
+/* Tuning and instrumentation knobs for paged_attn_decode_ex.  Zero-initialise
+ * and set what you need; a NULL options pointer means all defaults. */
+typedef struct pa_options {
+    /* Sequences with seq_len <= single_pass_max_len run in one pass (one
+     * workgroup per (sequence, KV head), output written directly); longer ones
+     * are partitioned.  < 0: automatic (8192 tokens when num_seqs*num_kv_heads
+     * is at least 4 x num_cus, otherwise one partition); 0: partition every
+     * sequence (phase 2 always runs). */
+    int single_pass_max_len;
+    /* Compute units assumed by the automatic choices; <= 0 means 256 (MI355X). */
+    int num_cus;
+    int reserved[6];
+    /* If non-NULL, hipEventRecord(phase1_begin/phase1_end, stream) is issued
+     * immediately before/after the phase-1 kernel (instrumentation only). */
+    hipEvent_t phase1_begin;
+    hipEvent_t phase1_end;
+} pa_options;
+
+/* What a call will launch; filled by paged_attn_plan. */
+typedef struct pa_plan_info {
+    int partition_size;        /* resolved partition size, tokens           */
+    int single_pass_max_len;   /* resolved tier threshold, tokens           */
+    int max_partitions;        /* partitions per (sequence, KV head) slot   */
+    int group;                 /* query heads per KV head                   */
+    long long phase1_workgroups;   /* grid of the phase-1 kernel            */
+    long long phase2_workgroups;   /* grid of the phase-2 kernel (0 = none) */
+    long long active_workgroups;   /* phase-1 workgroups that do work (needs host lengths) */
+    int single_pass_seqs;      /* sequences served in one pass (needs host lengths) */
+    int partitioned_seqs;      /* sequences split into partitions (needs host lengths) */
+    size_t workspace_bytes;    /* bytes of workspace the call needs         */
+    int threads_per_workgroup; /* phase-1 block size                        */
+    int lds_bytes_phase1;      /* static LDS of the phase-1 kernel          */
+} pa_plan_info;
+
+/*
+ * Bytes of device workspace paged_attn_decode needs for these sizes (0 when every
+ * sequence can run in a single pass).  max_seq_len <= 0 means "unknown", and the
+ * table capacity max_blocks_per_seq*block_size is used.  Returns (size_t)-1 for
+ * arguments paged_attn_decode would reject.
+ *
+ * The workspace holds, for each (sequence, query head, partition), the phase-1
+ * partial: weighted_v as head_dim fp32 values, then (max_score, exp_sum) as two
+ * fp32 values, with max_score in base-2 units (log2(e)*scale*q.k).
+ */
+size_t paged_attn_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                 int block_size, int max_blocks_per_seq, int max_seq_len,
+                                 int partition_size);
+
+size_t paged_attn_workspace_size_ex(int num_seqs, int num_heads, int num_kv_heads,
+                                    int head_dim, int block_size, int max_blocks_per_seq,
+                                    int max_seq_len, int partition_size,
+                                    const pa_options* opt);
+
+/*
+ * Decode attention for one step of a batch (the whole hot path: phase 1 with the
+ * length-tiered dispatch, then phase 2 for partitioned sequences).
+ *
+ *   out                 [num_seqs][num_heads][head_dim] dtype, written (device)
+ *   q                   [num_seqs][num_heads][head_dim] dtype (device)
+ *   key_cache/value_cache  paged caches, layout above (device)
+ *   block_tables        [num_seqs][max_blocks_per_seq] int32 (device)
+ *   seq_lens            [num_seqs] int32 (device); seq_len <= 0 gives a zero row.
+ *                       Values above max_seq_len are treated as max_seq_len.
+ *   num_seqs            >= 0 (0 is a no-op)
+ *   num_heads, num_kv_heads   query and KV heads; num_heads % num_kv_heads == 0
+ *   head_dim, block_size      see "Supported shapes"
+ *   scale               multiplies q.k in fp32 (typically 1/sqrt(head_dim))
+ *   partition_size      tokens per phase-1 partition of a long sequence; 0 = 512
+ *   workspace           device scratch of workspace_bytes bytes (may be NULL when
+ *                       paged_attn_workspace_size(...) == 0); not read before written
+ *   stream              hipStream_t to enqueue on
+ *   max_blocks_per_seq  row stride of block_tables (entries)
+ *   max_seq_len         host-known upper bound of seq_lens; <= 0 means
+ *                       max_blocks_per_seq*block_size.  Sizes the grid.
+ *   dtype               pa_dtype_t of q, the caches and out
+ *   workspace_bytes     size of workspace, checked against the requirement
+ * Returns PA_OK or the first error found.
+ */
+int paged_attn_decode(void* out, const void* q, const void* key_cache, const void* value_cache,
+                      const int32_t* block_tables, const int32_t* seq_lens, int num_seqs,
+                      int num_heads, int num_kv_heads, int head_dim, int block_size,
+                      float scale, int partition_size, void* workspace, hipStream_t stream,
+                      int max_blocks_per_seq, int max_seq_len, int dtype,
+                      size_t workspace_bytes);
+
+/* paged_attn_decode with tuning/instrumentation options (opt may be NULL). */
+int paged_attn_decode_ex(void* out, const void* q, const void* key_cache,
+                         const void* value_cache, const int32_t* block_tables,
+                         const int32_t* seq_lens, int num_seqs, int num_heads,
+                         int num_kv_heads, int head_dim, int block_size, float scale,
+                         int partition_size, void* workspace, hipStream_t stream,
+                         int max_blocks_per_seq, int max_seq_len, int dtype,
+                         size_t workspace_bytes, const pa_options* opt);
+
+/* Human-readable text for a pa_status_t (static storage, never NULL). */
+const char* paged_attn_status_str(int status);
+
+/*
+ * Host-only planning (no HIP call, usable without a GPU): fills *info with the
+ * grid, tier threshold, partition size and workspace a decode call with the same
+ * arguments would use.  seq_lens_host (host pointer, may be NULL) adds the
+ * per-sequence tier counts and the number of phase-1 workgroups that do work.
+ * Returns the status paged_attn_decode would return from validation
+ * (pointer arguments excepted).
+ */
+int paged_attn_plan(const int32_t* seq_lens_host, int num_seqs, int num_heads,
+                    int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                    int max_seq_len, int partition_size, int dtype, const pa_options* opt,
+                    pa_plan_info* info);
+
+/*
+ * Test hook for the block-table gather (the addressing and 16-byte page loads of
+ * phase 1, without the attention math): writes the K and V rows of tokens
+ * t < seq_lens[s] to k_out/v_out, laid out [num_seqs][num_kv_heads][max_seq_len]
+ * [head_dim] (16-bit elements copied bit for bit; other slots are not written).
+ * max_seq_len must be > 0 and <= max_blocks_per_seq*block_size.
+ */
+int paged_attn_gather_probe(void* k_out, void* v_out, const void* key_cache,
+                            const void* value_cache, const int32_t* block_tables,
+                            const int32_t* seq_lens, int num_seqs, int num_kv_heads,
+                            int head_dim, int block_size, int max_blocks_per_seq,
+                            int max_seq_len, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

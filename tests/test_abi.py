@@ -1,0 +1,162 @@
+"""C-ABI boundary and host planner tests (CPU only: no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gqa_aware_paged_amd as pa
+from gqa_aware_paged_amd import build as pa_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "pages_design_sizes.txt")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if pa_build.is_stale():
+        pa_build.build()
+    return pa.lib()
+
+
+def golden():
+    vals = {}
+    for line in open(GOLDEN):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            k, v = line.split("=")
+            vals[k.strip()] = int(v)
+    return vals
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(paged_attn_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert len(names) >= 7
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(pa.SYMBOLS)
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = lib.paged_attn_status_str(code).decode()
+        assert s.startswith("PA_")
+    assert "unknown" in lib.paged_attn_status_str(99).decode()
+
+
+FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced: every call below fails validation
+
+
+def call(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, S=2, Hq=24, Hkv=4, D=256, bs=16,
+             scale=0.0625, P=512, ws=None, stream=None, mbps=64, maxlen=0, dtype=0, wsb=0)
+    a.update(kw)
+    return lib.paged_attn_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["sl"], a["S"],
+                                 a["Hq"], a["Hkv"], a["D"], a["bs"], a["scale"], a["P"], a["ws"],
+                                 a["stream"], a["mbps"], a["maxlen"], a["dtype"], a["wsb"])
+
+
+def test_validation_errors_before_any_launch(lib):
+    # S=2, Hkv=4 -> small batch -> every sequence longer than one partition is split,
+    # so a workspace is required and the calls below stop at validation.
+    assert call(lib, q=None) == 1                    # PA_ERR_NULL
+    assert call(lib, Hkv=5) == 2                     # 24 % 5 -> PA_ERR_SHAPE
+    assert call(lib, D=96) == 3                      # PA_ERR_UNSUPPORTED
+    assert call(lib, Hq=68, Hkv=4) == 3              # group 17 > 16
+    assert call(lib, bs=8) == 3                      # block size not a multiple of 16
+    assert call(lib, dtype=2) == 3
+    assert call(lib, P=24) == 4                      # PA_ERR_PARTITION
+    assert call(lib, P=-16) == 4
+    assert call(lib, maxlen=64 * 16 + 1) == 2        # longer than the table row
+    assert call(lib, scale=float("nan")) == 2
+    assert call(lib) == 5                            # workspace missing -> PA_ERR_WORKSPACE
+    need = lib.paged_attn_workspace_size(2, 24, 4, 256, 16, 64, 0, 512)
+    assert call(lib, ws=FAKE, wsb=need - 1) == 5
+    assert call(lib, ws=ctypes.c_void_p(0x10010), wsb=need) == 7    # workspace not 256-B aligned
+    assert call(lib, q=ctypes.c_void_p(0x10008)) == 7               # q not 16-B aligned
+    assert call(lib, S=0) == 0                                      # empty batch: no-op
+
+
+def test_workspace_size_formula(lib):
+    S, Hq, Hkv, D, bs, mbps, P = 4, 24, 4, 256, 16, 6400, 512
+    n = lib.paged_attn_workspace_size(S, Hq, Hkv, D, bs, mbps, 102400, P)
+    parts = 102400 // P
+    acc = S * Hq * parts * D * 4
+    assert n == ((acc + 255) // 256) * 256 + S * Hq * parts * 8
+    # a batch big enough to fill the GPU keeps sequences <= 8192 in one pass: no workspace
+    assert lib.paged_attn_workspace_size(256, 24, 4, 256, 16, 512, 8192, 512) == 0
+    assert lib.paged_attn_workspace_size(2, 24, 5, 256, 16, 64, 0, 512) == ctypes.c_size_t(-1).value
+
+
+def test_plan_matches_pages_grid(lib):
+    """One 100K-token sequence with 512-token partitions: 200 partitions and a grid
+    of 4 KV heads x 200 = 800 workgroups instead of 24 x 200 = 4800."""
+    g = golden()
+    L, P = g["long_seq_tokens"], g["partition_size"]
+    info = pa.plan([L], g["num_q_heads"], g["num_kv_heads"], g["tile_head_dim"], 16,
+                   L // 16, L, P, single_pass_max_len=0)
+    assert info["max_partitions"] == g["num_partitions"]
+    assert info["phase1_workgroups"] == g["blocks_per_kv_head_grid"]
+    assert info["phase1_workgroups"] * info["group"] == g["blocks_per_q_head_grid"]
+    assert info["group"] == g["gqa_ratio"] == g["kv_reads_saved_factor"]
+    assert info["active_workgroups"] == 800
+    assert info["partitioned_seqs"] == 1
+    # the same arithmetic for the 4-sequence long-context workload
+    info4 = pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, P)
+    assert info4["phase1_workgroups"] == 3200 and info4["phase2_workgroups"] == 4 * 4 * 8
+
+
+def test_tier_thresholds(lib):
+    g = golden()
+    # big batch (S*Hkv >= 4*256): the pages' single-pass bound of 8192 tokens
+    lens = [g["single_pass_max_len"]] * 256 + [g["single_pass_max_len"] + 1] * 8
+    info = pa.plan(lens, 24, 4, 256, 16, 1024, 0, 512)
+    assert info["single_pass_max_len"] == g["single_pass_max_len"]
+    assert info["single_pass_seqs"] == 256 and info["partitioned_seqs"] == 8
+    # small batch on 256 CUs: anything longer than one partition is split
+    info = pa.plan([512, 513, 8192], 24, 4, 256, 16, 512, 0, 512)
+    assert info["single_pass_max_len"] == 512
+    assert info["single_pass_seqs"] == 1 and info["partitioned_seqs"] == 2
+    assert info["active_workgroups"] == 4 * (1 + 2 + 16)
+    # explicit threshold and partition sizes
+    for P in (256, 512, 1024):
+        info = pa.plan([65536], 24, 4, 256, 16, 4096, 65536, P, single_pass_max_len=8192)
+        assert info["max_partitions"] == 65536 // P
+    info = pa.plan([100, 0, 7], 24, 4, 256, 16, 8, 100, 0, single_pass_max_len=100)
+    assert info["single_pass_seqs"] == 3 and info["phase2_workgroups"] == 0
+    assert info["partition_size"] == 512
+
+
+def test_tile_budget_against_pages(lib):
+    """The pages size K and V tiles of 32 x 256 fp16 at 16 KB each, 32 KB of the
+    48 KB SMEM budget.  Here each wave stages 16-token K and V tiles (8 KB each);
+    four waves fill 64 KB of gfx950's 160 KB LDS, so two workgroups fit per CU."""
+    g = golden()
+    assert g["k_tile_tokens"] * g["tile_head_dim"] * 2 == g["k_tile_bytes_f16"]
+    assert 2 * g["k_tile_bytes_f16"] == g["kv_tile_bytes_f16"] <= g["smem_budget_bytes"]
+    assert g["gqa_ratio"] * g["tile_head_dim"] == g["group_live_registers"]
+    info = pa.plan([1024], 24, 4, 256, 16, 64)
+    assert info["lds_bytes_phase1"] == 4 * 2 * 16 * 256 * 2 == 65536
+    assert 2 * (info["lds_bytes_phase1"] + 16 * 256 * 2) <= 160 * 1024
+    assert info["threads_per_workgroup"] == 256
+
+
+def test_plan_rejects_what_decode_rejects(lib):
+    with pytest.raises(pa.PagedAttnError, match="PARTITION"):
+        pa.plan([10], 24, 4, 256, 16, 4, 0, 40)
+    with pytest.raises(pa.PagedAttnError, match="UNSUPPORTED"):
+        pa.plan([10], 24, 4, 64, 16, 4, 0, 512)
+
+
+def test_product_path_has_no_oracle_or_fallback():
+    """The package never imports the oracle and fails loudly without its library."""
+    src = open(os.path.join(ROOT, "gqa_aware_paged_amd", "__init__.py")).read()
+    assert "oracle" not in src.replace("no fallback", "")
+    assert "raise RuntimeError" in src
