@@ -104,7 +104,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long",
                     choices=["tiny", "batch", "long", "mixed", "saturation"])
-    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--partition-size", type=int, default=0,
+                    help="tokens per partition; 0 = automatic (one workgroup per CU)")
+    ap.add_argument("--skip-p512", action="store_true",
+                    help="skip the extra timing at the pages' 512-token partitions")
     ap.add_argument("--single-pass-max-len", type=int, default=None)
     ap.add_argument("--cpu-seqs", type=int, default=4,
                     help="sequences of the workload the CPU oracle is timed on")
@@ -130,16 +133,16 @@ def main():
     pa.lib()
 
     log(f"generating workload {args.workload}")
-    kw = {}
-    if args.partition_size is not None and args.workload == "mixed":
-        kw["partition_size"] = args.partition_size
-    w = workloads.NAMED[args.workload](device="cuda", **kw)
-    P = args.partition_size if args.partition_size is not None else w.partition_size
+    w = workloads.NAMED[args.workload](device="cuda")
     torch.cuda.synchronize()
 
-    dec = pa.Decoder(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size,
-                     w.max_blocks_per_seq, w.q.dtype, max_seq_len=w.max_seq_len,
-                     partition_size=P, single_pass_max_len=args.single_pass_max_len)
+    def decoder(P):
+        return pa.Decoder(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                          w.max_blocks_per_seq, w.q.dtype, max_seq_len=w.max_seq_len,
+                          partition_size=P, single_pass_max_len=args.single_pass_max_len)
+
+    P = args.partition_size
+    dec = decoder(P)
     info = pa.plan(list(w.seq_lens_host), w.num_heads, w.num_kv_heads, w.head_dim,
                    w.block_size, w.max_blocks_per_seq, w.max_seq_len, P,
                    single_pass_max_len=args.single_pass_max_len)
@@ -157,30 +160,55 @@ def main():
 
     ev = HipEvents()
     stream = torch.cuda.current_stream(dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def step(d, events=None):
+        d(w.q, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, w.scale, events=events)
+
+    def timed(d, n, with_events=False):
+        """n back-to-back steps between events on the launch stream; returns ms/step and,
+        with_events, the phase-1 durations (ms) from HIP events around each launch."""
+        pairs = [(ev.create(), ev.create()) for _ in range(n)] if with_events else None
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(n):
+            step(d, pairs[i] if pairs else None)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / n
+        ph1 = None
+        if pairs:
+            ph1 = [ev.elapsed_ms(a, b) for a, b in pairs]
+            for a, b in pairs:
+                ev.destroy(a)
+                ev.destroy(b)
+        return ms, ph1
+
     for _ in range(args.warmup):
-        dec(w.q, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, w.scale)
+        step(dec)
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
-    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # timed region 1: K plain steps -> ms_per_step
     t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        dec(w.q, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, w.scale,
-            events=pairs[i])
-    stop.record(stream)
-    torch.cuda.synchronize()
+    step_ms, _ = timed(dec, args.steps)
     wall = time.perf_counter() - t0
-    step_ms = start.elapsed_time(stop) / args.steps
-    ph1 = sorted(ev.elapsed_ms(a, b) for a, b in pairs)
-    for a, b in pairs:
-        ev.destroy(a)
-        ev.destroy(b)
+    # timed region 2: K steps with HIP events around each phase-1 launch
+    step_ms_ev, ph1 = timed(dec, args.steps, with_events=True)
+    ph1 = sorted(ph1)
     ph1_avg = sum(ph1) / len(ph1)
-    log(f"timed {args.steps} steps: {step_ms * 1e3:.1f} us/step (wall {wall:.3f} s), "
-        f"phase-1 avg {ph1_avg * 1e3:.1f} us, median {ph1[len(ph1) // 2] * 1e3:.1f} us")
+    log(f"timed {args.steps} steps: {step_ms * 1e3:.1f} us/step (wall {wall:.3f} s); with "
+        f"phase-1 events {step_ms_ev * 1e3:.1f} us/step, phase-1 avg {ph1_avg * 1e3:.1f} us, "
+        f"median {ph1[len(ph1) // 2] * 1e3:.1f} us")
+    # context: the pages' fixed 512-token partitions on the same inputs
+    p512_ms = None
+    if P != 512 and not args.skip_p512:
+        d512 = decoder(512)
+        for _ in range(args.warmup):
+            step(d512)
+        p512_ms, _ = timed(d512, args.steps)
+        log(f"partition_size=512: {p512_ms * 1e3:.1f} us/step")
+        del d512
 
     # algorithmic bytes: one unit = one (token, KV head); it reads a K row and a V row
     units = int(w.seq_lens_host.clip(0).astype("int64").sum()) * w.num_kv_heads
@@ -199,6 +227,7 @@ def main():
         "ms_per_step": round(step_ms, 5),
         "us_per_step": round(step_ms * 1e3, 2),
         "pct_hbm_peak": round(100 * eff / HBM_PEAK_GBS, 2),
+        "us_per_step_partition_512": None if p512_ms is None else round(p512_ms * 1e3, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -208,7 +237,9 @@ def main():
                    "seq_lens": "all 102400" if args.workload == "long" else
                    f"{int(w.seq_lens_host.min())}..{int(w.seq_lens_host.max())}",
                    "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
-                   "head_dim": w.head_dim, "block_size": w.block_size, "partition_size": P,
+                   "head_dim": w.head_dim, "block_size": w.block_size,
+                   "partition_size": info["partition_size"],
+                   "partition_size_arg": P,
                    "single_pass_max_len": info["single_pass_max_len"],
                    "kv_bytes_per_step": kv, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "pa_phase1_kernel",

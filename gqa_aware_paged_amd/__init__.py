@@ -25,8 +25,8 @@ SYMBOLS = ("paged_attn_workspace_size", "paged_attn_workspace_size_ex", "paged_a
 
 class Options(ctypes.Structure):
     _fields_ = [("single_pass_max_len", ctypes.c_int), ("num_cus", ctypes.c_int),
-                ("reserved", ctypes.c_int * 6), ("phase1_begin", ctypes.c_void_p),
-                ("phase1_end", ctypes.c_void_p)]
+                ("total_tokens_hint", ctypes.c_longlong), ("reserved", ctypes.c_int * 4),
+                ("phase1_begin", ctypes.c_void_p), ("phase1_end", ctypes.c_void_p)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -86,10 +86,11 @@ def _check(status: int):
 
 
 def _opts(single_pass_max_len: Optional[int], num_cus: int = 0,
-          events: Optional[Tuple[int, int]] = None) -> Options:
+          events: Optional[Tuple[int, int]] = None, total_tokens_hint: int = 0) -> Options:
     o = Options()
     o.single_pass_max_len = -1 if single_pass_max_len is None else int(single_pass_max_len)
     o.num_cus = int(num_cus)
+    o.total_tokens_hint = int(total_tokens_hint)
     if events is not None:
         o.phase1_begin, o.phase1_end = events
     return o
@@ -102,7 +103,7 @@ def _ptr(t: Optional[torch.Tensor]):
 def plan(seq_lens_host, num_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
          max_blocks_per_seq: int, max_seq_len: int = 0, partition_size: int = 0,
          dtype: int = PA_F16, single_pass_max_len: Optional[int] = None,
-         num_seqs: Optional[int] = None, num_cus: int = 0) -> dict:
+         num_seqs: Optional[int] = None, num_cus: int = 0, total_tokens_hint: int = 0) -> dict:
     """Host-only plan (no GPU needed).  seq_lens_host: sequence of ints or None."""
     arr = None
     if seq_lens_host is not None:
@@ -110,7 +111,7 @@ def plan(seq_lens_host, num_heads: int, num_kv_heads: int, head_dim: int, block_
         arr = (ctypes.c_int32 * n)(*[int(x) for x in seq_lens_host])
         num_seqs = n
     info = PlanInfo()
-    o = _opts(single_pass_max_len, num_cus)
+    o = _opts(single_pass_max_len, num_cus, total_tokens_hint=total_tokens_hint)
     _check(lib().paged_attn_plan(arr, int(num_seqs or 0), num_heads, num_kv_heads, head_dim,
                                  block_size, max_blocks_per_seq, max_seq_len, partition_size,
                                  dtype, ctypes.byref(o), ctypes.byref(info)))
@@ -119,8 +120,9 @@ def plan(seq_lens_host, num_heads: int, num_kv_heads: int, head_dim: int, block_
 
 def workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
                    block_size: int, max_blocks_per_seq: int, max_seq_len: int = 0,
-                   partition_size: int = 0, single_pass_max_len: Optional[int] = None) -> int:
-    o = _opts(single_pass_max_len)
+                   partition_size: int = 0, single_pass_max_len: Optional[int] = None,
+                   total_tokens_hint: int = 0) -> int:
+    o = _opts(single_pass_max_len, total_tokens_hint=total_tokens_hint)
     n = lib().paged_attn_workspace_size_ex(num_seqs, num_heads, num_kv_heads, head_dim,
                                            block_size, max_blocks_per_seq, max_seq_len,
                                            partition_size, ctypes.byref(o))
@@ -139,16 +141,17 @@ class Decoder:
     def __init__(self, num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
                  block_size: int, max_blocks_per_seq: int, dtype: torch.dtype,
                  max_seq_len: int = 0, partition_size: int = 0,
-                 single_pass_max_len: Optional[int] = None, device="cuda"):
+                 single_pass_max_len: Optional[int] = None, total_tokens_hint: int = 0,
+                 device="cuda"):
         self.shape = (num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                       max_blocks_per_seq)
         self.dtype = dtype
         self.max_seq_len = int(max_seq_len)
         self.partition_size = int(partition_size)
-        self.opts = _opts(single_pass_max_len)
+        self.opts = _opts(single_pass_max_len, total_tokens_hint=total_tokens_hint)
         nbytes = workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                                 max_blocks_per_seq, max_seq_len, partition_size,
-                                single_pass_max_len)
+                                single_pass_max_len, total_tokens_hint)
         self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
         self.workspace_bytes = nbytes
         self.out = torch.empty((num_seqs, num_heads, head_dim), dtype=dtype, device=device)
@@ -191,19 +194,19 @@ def decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
            block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
            partition_size: int = 0, max_seq_len: int = 0, out: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None, single_pass_max_len: Optional[int] = None,
-           events: Optional[Tuple[int, int]] = None) -> torch.Tensor:
+           events: Optional[Tuple[int, int]] = None, total_tokens_hint: int = 0) -> torch.Tensor:
     """One decode step: out[s,h] = softmax(scale q K^T) V over the paged caches."""
     _validate(q, key_cache, value_cache, block_tables, seq_lens)
     S, Hq, D = q.shape
     _, Hkv, bs, _ = key_cache.shape
     mbps = block_tables.shape[1]
     need = workspace_size(S, Hq, Hkv, D, bs, mbps, max_seq_len, partition_size,
-                          single_pass_max_len)
+                          single_pass_max_len, total_tokens_hint)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty_like(q)
-    o = _opts(single_pass_max_len, events=events)
+    o = _opts(single_pass_max_len, events=events, total_tokens_hint=total_tokens_hint)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(lib().paged_attn_decode_ex(
         _ptr(out), _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),

@@ -19,7 +19,7 @@
 // (single-pass tier) or the partition's compound partial (page of commit
 // 8d26e23: max_score, exp_sum, weighted_v).
 //
-// Phase 2 (pa_reduce_kernel): one workgroup per (sequence, KV head, 32-wide
+// Phase 2 (pa_reduce_kernel): one workgroup per (sequence, KV head, 16-wide
 // slice of head_dim) merges the partials of all partitions for the group's
 // query heads with the rescale of the online-softmax fix (page of commit
 // 87a19d2): M = max_p m_p, w_p = l_p 2^(m_p - M), out = sum_p w_p acc_p / sum_p w_p.
@@ -140,6 +140,14 @@ __device__ __forceinline__ bool workgroup_span(int L, int part, int P, int T1, S
   return true;
 }
 
+// Workspace layout of the normalised partition outputs: [S*Hq][D/16][max_parts][16]
+// floats, so the partitions of one 16-wide slice are contiguous (phase 2 reads
+// 1 KiB runs) and phase 1 writes 64-byte runs.
+__device__ __forceinline__ size_t ws_acc_index(size_t row, int c, int max_parts, int part,
+                                               int D) {
+  return ((row * (D / 16) + c) * max_parts + part) * 16;
+}
+
 // Element offset of token t0 (a multiple of 16) of KV head kvh of sequence s.
 // 64-bit: pools above 4 G elements are legal.  The page id is wave-uniform.
 __device__ __forceinline__ size_t tile_offset(const int32_t* bt, int s, int t0, int kvh,
@@ -150,12 +158,14 @@ __device__ __forceinline__ size_t tile_offset(const int32_t* bt, int s, int t0, 
 
 // One 16-token tile is 16*D*2 bytes, contiguous.  Lane `lane` fetches the 16-byte
 // chunks lane, lane+64, ... so every load instruction covers 1 KiB contiguously.
+// K and V are read exactly once per step, so the loads are nontemporal: they do
+// not displace reusable lines from the caches (worth ~10% of gather bandwidth).
 template <int D>
 __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ src, int lane,
                                           u32x4 (&r)[D / 32]) {
   const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
 #pragma unroll
-  for (int j = 0; j < D / 32; ++j) r[j] = s4[j * 64 + lane];
+  for (int j = 0; j < D / 32; ++j) r[j] = __builtin_nontemporal_load(s4 + j * 64 + lane);
 }
 
 // LDS slot of one tile: 16 rows of D halves, with 16-byte chunk c of row t stored
@@ -217,6 +227,17 @@ __global__ __launch_bounds__(W * 64, 2) void pa_phase1_kernel(DecodeArgs a) {
   const int col = lane & 15;     // query head (QK^T/PV columns) or row index within a tile
   const int grp = lane >> 4;     // 4-lane-group index: k-slot block / 4-row block
 
+  // the wave's first tile is requested before Q is staged, so the two latencies overlap
+  const int n_tiles = (sp.t_end - sp.t_begin + kTile - 1) / kTile;
+  u32x4 rk[LOADS], rv[LOADS];
+  int it = wave;
+  if (it < n_tiles) {
+    const size_t off = tile_offset(a.bt, s, sp.t_begin + kTile * it, kvh, Hkv, a.block_size,
+                                   a.max_blocks_per_seq, D);
+    load_tile<D>(a.kc + off, lane, rk);
+    load_tile<D>(a.vc + off, lane, rv);
+  }
+
   // Q of the group, staged once in LDS as the B operand of S^T = K Q^T: row h is
   // query head kvh*G + h (rows G..15 are zero), swizzled like a K tile.
   {
@@ -238,16 +259,6 @@ __global__ __launch_bounds__(W * 64, 2) void pa_phase1_kernel(DecodeArgs a) {
 
   unsigned char* ldsK = lds + wave * 2 * TILE_BYTES;
   unsigned char* ldsV = ldsK + TILE_BYTES;
-  const int n_tiles = (sp.t_end - sp.t_begin + kTile - 1) / kTile;
-
-  u32x4 rk[LOADS], rv[LOADS];
-  int it = wave;
-  if (it < n_tiles) {
-    const size_t off = tile_offset(a.bt, s, sp.t_begin + kTile * it, kvh, Hkv, a.block_size,
-                                   a.max_blocks_per_seq, D);
-    load_tile<D>(a.kc + off, lane, rk);
-    load_tile<D>(a.vc + off, lane, rv);
-  }
 
   for (; it < n_tiles; it += W) {
     const int t0 = sp.t_begin + kTile * it;
@@ -301,19 +312,28 @@ __global__ __launch_bounds__(W * 64, 2) void pa_phase1_kernel(DecodeArgs a) {
     l_run = l_run * alpha + psum;
     const u32x2 pop = {pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
 
-    // O^T[d, head] += sum_t V[t, d] P[head, t]; A operand = V^T read column-wise
+    // O^T[d, head] += sum_t V[t, d] P[head, t].  The A operand (lane: dim 16c + col,
+    // tokens 4*grp .. +3) is V^T; ds_read_b64_tr_b16 transposes it out of the
+    // row-major tile: within each 16-lane group, result lane i, element j comes
+    // from source lane i/4 + 4j, element i%4, so source lane r addresses row
+    // 4*grp + r/4, columns 16c + 4*(r%4) .. +3.
     const bool tail = t0 + kTile > sp.t_end;
+    uint32_t keep_lo = 0xffffffffu, keep_hi = 0xffffffffu;   // masks slots past the end
+    if (tail) {
+      const int n = sp.t_end - tk;                              // valid tokens of this lane
+      keep_lo = (n > 0 ? 0x0000ffffu : 0u) | (n > 1 ? 0xffff0000u : 0u);
+      keep_hi = (n > 2 ? 0x0000ffffu : 0u) | (n > 3 ? 0xffff0000u : 0u);
+    }
+    const int vrow = 4 * grp + (col >> 2);
 #pragma unroll
     for (int c = 0; c < DB; ++c) {
-      const int d = 16 * c + col;
-      uint32_t v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 4 * grp + e;
-        v[e] = *reinterpret_cast<const uint16_t*>(ldsV + Z::byte_off(row, d >> 3) + (d & 7) * 2);
-        if (tail && t0 + row >= sp.t_end) v[e] = 0;   // slots past the end may hold NaN
-      }
-      const u32x2 vop = {v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
+      const int vcol = 16 * c + 4 * (col & 3);
+      typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+      const i16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(ldsV + Z::byte_off(vrow, vcol >> 3) + (vcol & 7) * 2));
+      u32x2 vop = __builtin_bit_cast(u32x2, raw);
+      vop.x &= keep_lo;
+      vop.y &= keep_hi;
       acc[c] = DT::mfma_pv(vop, pop, acc[c] * alpha);
     }
   }
@@ -365,32 +385,43 @@ __global__ __launch_bounds__(W * 64, 2) void pa_phase1_kernel(DecodeArgs a) {
       *reinterpret_cast<u32x2*>(o + 16 * c) = packed;
     }
   } else {
-    const size_t rec = ((size_t)s * Hq + hq) * a.max_parts + part;
-    float* o = a.ws_acc + rec * D + 4 * grp;
+    const size_t row = (size_t)s * Hq + hq;
 #pragma unroll
-    for (int c = 0; c < DB; ++c) *reinterpret_cast<f32x4*>(o + 16 * c) = acc[c] * inv;
-    if (grp == 0) a.ws_ml[rec] = make_float2(M, Lsum);
+    for (int c = 0; c < DB; ++c)
+      *reinterpret_cast<f32x4*>(a.ws_acc + ws_acc_index(row, c, a.max_parts, part, D) +
+                                4 * grp) = acc[c] * inv;
+    if (grp == 0) a.ws_ml[row * a.max_parts + part] = make_float2(M, Lsum);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Phase 2: merge the partitions of every partitioned sequence.
 // ---------------------------------------------------------------------------
-constexpr int kRedSlice = 32;                 // head_dim values per workgroup
-constexpr int kRedQuads = kRedSlice / 4;      // float4 lanes per slice
+constexpr int kRedSlice = 16;                 // head_dim values per workgroup (one d-block)
+constexpr int kRedQuads = kRedSlice / 4;      // float4 lanes per slice (fastest in a wave)
 constexpr int kRedThreads = 256;
-constexpr int kRedGroups = kRedThreads / kRedQuads;   // partition groups
+constexpr int kRedWaves = kRedThreads / 64;
+constexpr int kRedGroups = kRedThreads / kRedQuads;   // partition groups (64)
 
-template <int D, class DT>
+// Workgroup (s, kvh, slice) merges the partitions of the G query heads of KV head
+// kvh for head_dim values [16*slice, +16).  G is a template parameter so all of
+// a round's loads (G heads x U partitions) are issued before any is consumed.
+//   pass 1: thread t reads (m_p, l_p) of partitions p = t + 256k of every head and
+//           keeps a running (max, sum of l 2^(m - max)); waves reduce by shuffles,
+//           then LDS gives every thread M_h and 1 / sum_p l_p 2^(m_p - M_h).
+//   pass 2: thread (pg, q4) accumulates l_p 2^(m_p - M_h) acc_p over p = pg + 64k;
+//           the 64 partition groups are reduced by shuffles (16 per wave) and LDS.
+template <int D, class DT, int G>
 __global__ __launch_bounds__(kRedThreads) void pa_reduce_kernel(DecodeArgs a) {
   constexpr int NSL = D / kRedSlice;
-  extern __shared__ f32x4 red[];                // [G][kRedGroups][kRedQuads]
-  __shared__ float sM[16], sW[16];
+  constexpr int U = G >= 16 ? 1 : (G >= 6 ? 2 : (G >= 3 ? 4 : 8));
+  __shared__ float red_m[kRedWaves][G], red_w[kRedWaves][G];
+  __shared__ f32x4 part_sum[kRedWaves][G][kRedQuads];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int Hkv = a.num_kv_heads, G = a.group, Hq = a.num_heads, MP = a.max_parts;
+  const int Hkv = a.num_kv_heads, Hq = a.num_heads, MP = a.max_parts;
   int wg = blockIdx.x;
   const int sl = wg % NSL;
   wg /= NSL;
@@ -400,53 +431,104 @@ __global__ __launch_bounds__(kRedThreads) void pa_reduce_kernel(DecodeArgs a) {
   const int L = min(a.seq_lens[s], a.max_seq_len);
   if (L <= a.single_pass_max_len) return;       // served in one pass by phase 1
   const int np = (L + a.partition_size - 1) / a.partition_size;
+  const size_t row0 = (size_t)s * Hq + (size_t)kvh * G;   // first query head of the group
+  const float2* ml0 = a.ws_ml + row0 * MP;
 
-  // per head: M = max_p m_p and Wsum = sum_p l_p 2^(m_p - M); one wave per head
-  for (int h = wave; h < G; h += kRedThreads / 64) {
-    const float2* ml = a.ws_ml + ((size_t)s * Hq + kvh * G + h) * MP;
-    float mx = kNegInf;
-    for (int p = lane; p < np; p += 64) mx = fmaxf(mx, ml[p].x);
+  // ---- pass 1: per-head max and weight sum
+  float mx[G], sm[G];
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) mx = xor_max(mx, m);
-    float sum = 0.f;
-    for (int p = lane; p < np; p += 64) sum += ml[p].y * __builtin_amdgcn_exp2f(ml[p].x - mx);
+  for (int h = 0; h < G; ++h) mx[h] = kNegInf, sm[h] = 0.f;
+  for (int p0 = 0; p0 < np; p0 += kRedThreads) {
+    const int p = p0 + tid;
+    const int pc = min(p, np - 1);               // always a valid record; masked below
+    float2 v[G];
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) sum = xor_add(sum, m);
-    if (lane == 0) {
-      sM[h] = mx;
-      sW[h] = sum;
+    for (int h = 0; h < G; ++h) v[h] = ml0[h * MP + pc];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float m = p < np ? v[h].x : kNegInf;
+      const float nm = fmaxf(mx[h], m);
+      const float sc = nm == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mx[h] - nm);
+      const float add = m == kNegInf ? 0.f : v[h].y * __builtin_amdgcn_exp2f(m - nm);
+      sm[h] = sm[h] * sc + add;
+      mx[h] = nm;
     }
   }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float m = mx[h];
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) m = xor_max(m, k);
+    float w = mx[h] == kNegInf ? 0.f : sm[h] * __builtin_amdgcn_exp2f(mx[h] - m);
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) w = xor_add(w, k);
+    if (lane == 0) red_m[wave][h] = m, red_w[wave][h] = w;
+  }
   __syncthreads();
+  float Mh[G], inv_w[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float m = red_m[0][h];
+#pragma unroll
+    for (int w = 1; w < kRedWaves; ++w) m = fmaxf(m, red_m[w][h]);
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kRedWaves; ++w)
+      t += red_m[w][h] == kNegInf ? 0.f : red_w[w][h] * __builtin_amdgcn_exp2f(red_m[w][h] - m);
+    Mh[h] = m;
+    inv_w[h] = 1.f / t;
+  }
 
-  const int dq = tid % kRedQuads;
+  // ---- pass 2: weighted sum of the normalised partition outputs
+  const int q4 = tid % kRedQuads;
   const int pg = tid / kRedQuads;
-  const int d0 = sl * kRedSlice + 4 * dq;
-  f32x4 acc[16];
+  f32x4 acc[G];
 #pragma unroll
-  for (int h = 0; h < 16; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int p = pg; p < np; p += kRedGroups) {
+  for (int h = 0; h < G; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int p0 = pg; p0 < np; p0 += kRedGroups * U) {
+    f32x4 v[G][U];
+    float2 m[G][U];
 #pragma unroll
-    for (int h = 0; h < 16; ++h) {
-      if (h < G) {
-        const size_t rec = ((size_t)s * Hq + kvh * G + h) * MP + p;
-        const float2 ml = a.ws_ml[rec];
-        const float w = ml.y * __builtin_amdgcn_exp2f(ml.x - sM[h]);
-        acc[h] += w * *reinterpret_cast<const f32x4*>(a.ws_acc + rec * D + d0);
+    for (int h = 0; h < G; ++h) {
+      const float* base = a.ws_acc + ws_acc_index(row0 + h, sl, MP, 0, D) + 4 * q4;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int pc = min(p0 + u * kRedGroups, np - 1);
+        m[h][u] = ml0[h * MP + pc];
+        v[h][u] = *reinterpret_cast<const f32x4*>(base + (size_t)pc * 16);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool ok = p0 + u * kRedGroups < np;
+        const float wgt = ok ? m[h][u].y * __builtin_amdgcn_exp2f(m[h][u].x - Mh[h]) : 0.f;
+        acc[h] += wgt * v[h][u];
       }
     }
   }
 #pragma unroll
-  for (int h = 0; h < 16; ++h)
-    if (h < G) red[(h * kRedGroups + pg) * kRedQuads + dq] = acc[h];
+  for (int h = 0; h < G; ++h) {
+    // reduce over the 16 partition groups of this wave (lane bits 2..5)
+#pragma unroll
+    for (int k = kRedQuads; k < 64; k <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[h][e] = xor_add(acc[h][e], k);
+    }
+    if (lane < kRedQuads) part_sum[wave][h][lane] = acc[h];
+  }
   __syncthreads();
   if (tid < G * kRedQuads) {
-    const int h = tid / kRedQuads, q4 = tid % kRedQuads;
-    f32x4 t = {0.f, 0.f, 0.f, 0.f};
-    for (int g = 0; g < kRedGroups; ++g) t += red[(h * kRedGroups + g) * kRedQuads + q4];
-    t *= 1.f / sW[h];
-    uint16_t* o = static_cast<uint16_t*>(a.out) + ((size_t)s * Hq + kvh * G + h) * D +
-                  sl * kRedSlice + 4 * q4;
+    const int h = tid / kRedQuads, qq = tid % kRedQuads;
+    f32x4 t = part_sum[0][h][qq];
+#pragma unroll
+    for (int w = 1; w < kRedWaves; ++w) t += part_sum[w][h][qq];
+    float iw = inv_w[0];
+#pragma unroll
+    for (int hh = 1; hh < G; ++hh) iw = hh == h ? inv_w[hh] : iw;
+    t *= iw;
+    uint16_t* o = static_cast<uint16_t*>(a.out) + (row0 + h) * D + sl * kRedSlice + 4 * qq;
     const u32x2 packed = {DT::bits(t[0]) | (DT::bits(t[1]) << 16),
                           DT::bits(t[2]) | (DT::bits(t[3]) << 16)};
     *reinterpret_cast<u32x2*>(o) = packed;

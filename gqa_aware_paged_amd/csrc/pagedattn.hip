@@ -6,7 +6,8 @@
 // a second kernel), re-thresholded for 256 compute units: one pass only pays
 // when the batch alone supplies enough workgroups; otherwise every sequence
 // longer than one partition is split.  The partition size is an argument, as
-// the page of commit 8d26e23 asks ("should be tunable"); 0 selects 512.
+// the page of commit 8d26e23 asks ("should be tunable"); 0 sizes partitions so
+// the step's K/V is spread over one workgroup per compute unit.
 #include "pagedattn.h"
 
 #include <hip/hip_runtime.h>
@@ -22,9 +23,8 @@
 namespace {
 
 constexpr int kWaves = 4;                   // waves per phase-1 workgroup
-constexpr int kDefaultPartition = 512;      // tokens
+constexpr int kMinAutoPartition = 256;     // tokens: smallest automatic partition
 constexpr int kDefaultCUs = 256;            // MI355X
-constexpr int kPagesSinglePassMax = 8192;   // one-pass bound when the batch fills the GPU
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct Plan {
@@ -55,20 +55,29 @@ int check_sizes(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, in
   return PA_OK;
 }
 
+// Partition size when the caller passes 0: spread the step's K/V over one
+// workgroup per compute unit.  The work estimate is num_seqs * max_seq_len tokens
+// per KV head (exact for equal lengths), or the caller's total-token hint.
+int auto_partition(long long S, int Hkv, int max_len, int cus, long long total_hint) {
+  const long long tokens = total_hint > 0 ? total_hint : S * max_len;
+  long long p = (tokens * Hkv + cus - 1) / cus;
+  p = (p + 15) / 16 * 16;
+  if (p < kMinAutoPartition) p = kMinAutoPartition;
+  if (p > max_len) p = (max_len + 15) / 16 * 16;
+  if (p < 16) p = 16;
+  return static_cast<int>(p);
+}
+
 int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int P_req,
               const pa_options* opt, Plan& pl) {
   pl = Plan{};
   pl.group = Hq / Hkv;
-  pl.P = P_req > 0 ? P_req : kDefaultPartition;
   pl.max_seq_len = max_len > 0 ? max_len : mbps * bs;
   const int cus = (opt && opt->num_cus > 0) ? opt->num_cus : kDefaultCUs;
-  if (opt && opt->single_pass_max_len >= 0) {
-    pl.T1 = opt->single_pass_max_len;
-  } else {
-    const long long slots = static_cast<long long>(S) * Hkv;
-    pl.T1 = slots >= 4LL * cus ? (kPagesSinglePassMax > pl.P ? kPagesSinglePassMax : pl.P)
-                               : pl.P;
-  }
+  const long long hint = opt ? opt->total_tokens_hint : 0;
+  pl.P = P_req > 0 ? P_req : auto_partition(S, Hkv, pl.max_seq_len, cus, hint);
+  // a sequence that fits in one partition is served in one pass
+  pl.T1 = (opt && opt->single_pass_max_len >= 0) ? opt->single_pass_max_len : pl.P;
   if (pl.max_seq_len > pl.T1) pl.max_parts = (pl.max_seq_len + pl.P - 1) / pl.P;
   const long long parts = pl.max_parts > 0 ? pl.max_parts : 1;
   pl.grid1 = static_cast<long long>(S) * Hkv * parts;
@@ -85,6 +94,37 @@ int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int 
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Phase 2 is instantiated per group size so its loads can all be in flight at once.
+template <int D, class DT, int G>
+void launch_reduce_g(unsigned grid, hipStream_t stream, const pa::DecodeArgs& args) {
+  hipLaunchKernelGGL((pa::pa_reduce_kernel<D, DT, G>), dim3(grid), dim3(pa::kRedThreads), 0,
+                     stream, args);
+}
+
+template <int D, class DT>
+int launch_reduce(int group, unsigned grid, hipStream_t stream, const pa::DecodeArgs& args) {
+  switch (group) {
+    case 1: launch_reduce_g<D, DT, 1>(grid, stream, args); break;
+    case 2: launch_reduce_g<D, DT, 2>(grid, stream, args); break;
+    case 3: launch_reduce_g<D, DT, 3>(grid, stream, args); break;
+    case 4: launch_reduce_g<D, DT, 4>(grid, stream, args); break;
+    case 5: launch_reduce_g<D, DT, 5>(grid, stream, args); break;
+    case 6: launch_reduce_g<D, DT, 6>(grid, stream, args); break;
+    case 7: launch_reduce_g<D, DT, 7>(grid, stream, args); break;
+    case 8: launch_reduce_g<D, DT, 8>(grid, stream, args); break;
+    case 9: launch_reduce_g<D, DT, 9>(grid, stream, args); break;
+    case 10: launch_reduce_g<D, DT, 10>(grid, stream, args); break;
+    case 11: launch_reduce_g<D, DT, 11>(grid, stream, args); break;
+    case 12: launch_reduce_g<D, DT, 12>(grid, stream, args); break;
+    case 13: launch_reduce_g<D, DT, 13>(grid, stream, args); break;
+    case 14: launch_reduce_g<D, DT, 14>(grid, stream, args); break;
+    case 15: launch_reduce_g<D, DT, 15>(grid, stream, args); break;
+    case 16: launch_reduce_g<D, DT, 16>(grid, stream, args); break;
+    default: return PA_ERR_UNSUPPORTED;
+  }
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 template <int D, class DT>
 int launch_decode(const pa::DecodeArgs& args, const Plan& pl, hipStream_t stream,
                   const pa_options* opt) {
@@ -98,10 +138,8 @@ int launch_decode(const pa::DecodeArgs& args, const Plan& pl, hipStream_t stream
     if (hipEventRecord(opt->phase1_end, stream) != hipSuccess) return PA_ERR_HIP;
   }
   if (pl.grid2 > 0) {
-    const size_t lds = static_cast<size_t>(pl.group) * pa::kRedGroups * pa::kRedQuads * 16;
-    hipLaunchKernelGGL((pa::pa_reduce_kernel<D, DT>), dim3(static_cast<unsigned>(pl.grid2)),
-                       dim3(pa::kRedThreads), lds, stream, args);
-    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+    const int st = launch_reduce<D, DT>(pl.group, static_cast<unsigned>(pl.grid2), stream, args);
+    if (st != PA_OK) return st;
   }
   return PA_OK;
 }

@@ -86,13 +86,16 @@ typedef enum pa_status_t {
 typedef struct pa_options {
     /* Sequences with seq_len <= single_pass_max_len run in one pass (one
      * workgroup per (sequence, KV head), output written directly); longer ones
-     * are partitioned.  < 0: automatic (8192 tokens when num_seqs*num_kv_heads
-     * is at least 4 x num_cus, otherwise one partition); 0: partition every
-     * sequence (phase 2 always runs). */
+     * are partitioned.  < 0: automatic (= the partition size: a sequence that fits
+     * in one partition is one pass); 0: partition every sequence (phase 2 always
+     * runs). */
     int single_pass_max_len;
     /* Compute units assumed by the automatic choices; <= 0 means 256 (MI355X). */
     int num_cus;
-    int reserved[6];
+    /* Sum of seq_lens if the caller knows it on the host (0 = unknown).  Only
+     * used to size automatic partitions for batches of unequal lengths. */
+    long long total_tokens_hint;
+    int reserved[4];
     /* If non-NULL, hipEventRecord(phase1_begin/phase1_end, stream) is issued
      * immediately before/after the phase-1 kernel (instrumentation only). */
     hipEvent_t phase1_begin;
@@ -148,7 +151,10 @@ size_t paged_attn_workspace_size_ex(int num_seqs, int num_heads, int num_kv_head
  *   num_heads, num_kv_heads   query and KV heads; num_heads % num_kv_heads == 0
  *   head_dim, block_size      see "Supported shapes"
  *   scale               multiplies q.k in fp32 (typically 1/sqrt(head_dim))
- *   partition_size      tokens per phase-1 partition of a long sequence; 0 = 512
+ *   partition_size      tokens per phase-1 partition of a long sequence (a positive
+ *                       multiple of 16), or 0: ceil(num_seqs * max_seq_len *
+ *                       num_kv_heads / 256) rounded up to 16, at least 256 and at
+ *                       most max_seq_len (one workgroup per compute unit)
  *   workspace           device scratch of workspace_bytes bytes (may be NULL when
  *                       paged_attn_workspace_size(...) == 0); not read before written
  *   stream              hipStream_t to enqueue on

@@ -90,8 +90,8 @@ def test_workspace_size_formula(lib):
     parts = 102400 // P
     acc = S * Hq * parts * D * 4
     assert n == ((acc + 255) // 256) * 256 + S * Hq * parts * 8
-    # a batch big enough to fill the GPU keeps sequences <= 8192 in one pass: no workspace
-    assert lib.paged_attn_workspace_size(256, 24, 4, 256, 16, 512, 8192, 512) == 0
+    # enough (sequence, KV head) pairs for every compute unit: one pass each, no workspace
+    assert lib.paged_attn_workspace_size(256, 24, 4, 256, 32, 512, 16384, 0) == 0
     assert lib.paged_attn_workspace_size(2, 24, 5, 256, 16, 64, 0, 512) == ctypes.c_size_t(-1).value
 
 
@@ -110,28 +110,49 @@ def test_plan_matches_pages_grid(lib):
     assert info["partitioned_seqs"] == 1
     # the same arithmetic for the 4-sequence long-context workload
     info4 = pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, P)
-    assert info4["phase1_workgroups"] == 3200 and info4["phase2_workgroups"] == 4 * 4 * 8
+    assert info4["phase1_workgroups"] == 3200 and info4["phase2_workgroups"] == 4 * 4 * 16
 
 
 def test_tier_thresholds(lib):
     g = golden()
-    # big batch (S*Hkv >= 4*256): the pages' single-pass bound of 8192 tokens
+    # explicit one-pass bound of 8192 tokens (the pages' short tier)
     lens = [g["single_pass_max_len"]] * 256 + [g["single_pass_max_len"] + 1] * 8
-    info = pa.plan(lens, 24, 4, 256, 16, 1024, 0, 512)
+    info = pa.plan(lens, 24, 4, 256, 16, 1024, 0, 512,
+                   single_pass_max_len=g["single_pass_max_len"])
     assert info["single_pass_max_len"] == g["single_pass_max_len"]
     assert info["single_pass_seqs"] == 256 and info["partitioned_seqs"] == 8
-    # small batch on 256 CUs: anything longer than one partition is split
+    # automatic tier: a sequence that fits in one partition runs in one pass
     info = pa.plan([512, 513, 8192], 24, 4, 256, 16, 512, 0, 512)
     assert info["single_pass_max_len"] == 512
     assert info["single_pass_seqs"] == 1 and info["partitioned_seqs"] == 2
     assert info["active_workgroups"] == 4 * (1 + 2 + 16)
-    # explicit threshold and partition sizes
+    # explicit partition sizes
     for P in (256, 512, 1024):
         info = pa.plan([65536], 24, 4, 256, 16, 4096, 65536, P, single_pass_max_len=8192)
         assert info["max_partitions"] == 65536 // P
     info = pa.plan([100, 0, 7], 24, 4, 256, 16, 8, 100, 0, single_pass_max_len=100)
     assert info["single_pass_seqs"] == 3 and info["phase2_workgroups"] == 0
-    assert info["partition_size"] == 512
+
+
+def test_automatic_partition_size_for_256_cus(lib):
+    """P = 0 spreads the step over one workgroup per compute unit."""
+    L = 102400
+    info = pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0)          # 4 x 100K tokens
+    assert info["partition_size"] == 6400 and info["phase1_workgroups"] == 256
+    info = pa.plan([L], 24, 4, 256, 16, L // 16, L, 0)              # one 100K sequence
+    assert info["partition_size"] == 1600 and info["phase1_workgroups"] == 256
+    info = pa.plan([16384] * 256, 24, 4, 256, 32, 512, 16384, 0)    # 1024 (seq, kv) pairs
+    assert info["partition_size"] == 16384 and info["partitioned_seqs"] == 0
+    assert info["phase2_workgroups"] == 0 and info["workspace_bytes"] == 0
+    info = pa.plan([100] * 8, 24, 4, 256, 16, 8, 100, 0)            # short: one pass, P >= 256
+    assert info["partition_size"] == 112 and info["single_pass_seqs"] == 8
+    # a host-side total shrinks the partitions of an unequal batch
+    lens = [64] * 60 + [65536] * 4
+    a = pa.plan(lens, 24, 4, 256, 16, 4096, 65536, 0)
+    b = pa.plan(lens, 24, 4, 256, 16, 4096, 65536, 0, total_tokens_hint=sum(lens))
+    per_cu = -(-sum(lens) * 4 // 256)
+    assert a["partition_size"] == 65536
+    assert b["partition_size"] == -(-per_cu // 16) * 16 and b["partitioned_seqs"] == 4
 
 
 def test_tile_budget_against_pages(lib):
