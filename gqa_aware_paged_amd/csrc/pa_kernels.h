@@ -22,7 +22,8 @@
 // Phase 2 (pa_reduce_kernel): one workgroup per (sequence, KV head, 16-wide
 // slice of head_dim) merges the partials of all partitions for the group's
 // query heads with the rescale of the online-softmax fix (page of commit
-// 87a19d2): M = max_p m_p, w_p = l_p 2^(m_p - M), out = sum_p w_p acc_p / sum_p w_p.
+// 87a19d2): with M the largest max, each partition weighs l_p 2^(m_p - M) and
+// out = sum_p weight_p acc_p / sum_p weight_p, evaluated as an associative fold.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -403,20 +404,35 @@ constexpr int kRedThreads = 256;
 constexpr int kRedWaves = kRedThreads / 64;
 constexpr int kRedGroups = kRedThreads / kRedQuads;   // partition groups (64)
 
+// Merge of two compound partials (m, w, a): m is a base-2 max, w the weight sum
+// and a the weighted sum, both relative to m.  (-inf, 0, 0) is the identity.
+struct Partial {
+  float m, w;
+  f32x4 a;
+};
+
+__device__ __forceinline__ void combine_into(Partial& x, float om, float ow, f32x4 oa) {
+  const float nm = fmaxf(x.m, om);
+  const float fx = nm == kNegInf ? 0.f : __builtin_amdgcn_exp2f(x.m - nm);
+  const float fo = nm == kNegInf ? 0.f : __builtin_amdgcn_exp2f(om - nm);
+  x.w = x.w * fx + ow * fo;
+  x.a = x.a * fx + oa * fo;
+  x.m = nm;
+}
+
 // Workgroup (s, kvh, slice) merges the partitions of the G query heads of KV head
-// kvh for head_dim values [16*slice, +16).  G is a template parameter so all of
-// a round's loads (G heads x U partitions) are issued before any is consumed.
-//   pass 1: thread t reads (m_p, l_p) of partitions p = t + 256k of every head and
-//           keeps a running (max, sum of l 2^(m - max)); waves reduce by shuffles,
-//           then LDS gives every thread M_h and 1 / sum_p l_p 2^(m_p - M_h).
-//   pass 2: thread (pg, q4) accumulates l_p 2^(m_p - M_h) acc_p over p = pg + 64k;
-//           the 64 partition groups are reduced by shuffles (16 per wave) and LDS.
+// kvh for head_dim values [16*slice, +16).  Thread (pg, q4) folds partitions
+// p = pg + 64k of every head into a running partial (the rescale rule of the
+// online-softmax fix), issuing all loads of a round (G heads x U partitions)
+// before consuming any; the 64 partition groups are then combined with the same
+// rule by lane shuffles (16 groups per wave) and through LDS (4 waves).  G is a
+// template parameter so the per-head state lives in registers.
 template <int D, class DT, int G>
 __global__ __launch_bounds__(kRedThreads) void pa_reduce_kernel(DecodeArgs a) {
   constexpr int NSL = D / kRedSlice;
   constexpr int U = G >= 16 ? 1 : (G >= 6 ? 2 : (G >= 3 ? 4 : 8));
-  __shared__ float red_m[kRedWaves][G], red_w[kRedWaves][G];
-  __shared__ f32x4 part_sum[kRedWaves][G][kRedQuads];
+  __shared__ float red_m[kRedWaves][G][kRedQuads], red_w[kRedWaves][G][kRedQuads];
+  __shared__ f32x4 red_a[kRedWaves][G][kRedQuads];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -434,57 +450,11 @@ __global__ __launch_bounds__(kRedThreads) void pa_reduce_kernel(DecodeArgs a) {
   const size_t row0 = (size_t)s * Hq + (size_t)kvh * G;   // first query head of the group
   const float2* ml0 = a.ws_ml + row0 * MP;
 
-  // ---- pass 1: per-head max and weight sum
-  float mx[G], sm[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) mx[h] = kNegInf, sm[h] = 0.f;
-  for (int p0 = 0; p0 < np; p0 += kRedThreads) {
-    const int p = p0 + tid;
-    const int pc = min(p, np - 1);               // always a valid record; masked below
-    float2 v[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) v[h] = ml0[h * MP + pc];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float m = p < np ? v[h].x : kNegInf;
-      const float nm = fmaxf(mx[h], m);
-      const float sc = nm == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mx[h] - nm);
-      const float add = m == kNegInf ? 0.f : v[h].y * __builtin_amdgcn_exp2f(m - nm);
-      sm[h] = sm[h] * sc + add;
-      mx[h] = nm;
-    }
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float m = mx[h];
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) m = xor_max(m, k);
-    float w = mx[h] == kNegInf ? 0.f : sm[h] * __builtin_amdgcn_exp2f(mx[h] - m);
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) w = xor_add(w, k);
-    if (lane == 0) red_m[wave][h] = m, red_w[wave][h] = w;
-  }
-  __syncthreads();
-  float Mh[G], inv_w[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float m = red_m[0][h];
-#pragma unroll
-    for (int w = 1; w < kRedWaves; ++w) m = fmaxf(m, red_m[w][h]);
-    float t = 0.f;
-#pragma unroll
-    for (int w = 0; w < kRedWaves; ++w)
-      t += red_m[w][h] == kNegInf ? 0.f : red_w[w][h] * __builtin_amdgcn_exp2f(red_m[w][h] - m);
-    Mh[h] = m;
-    inv_w[h] = 1.f / t;
-  }
-
-  // ---- pass 2: weighted sum of the normalised partition outputs
   const int q4 = tid % kRedQuads;
   const int pg = tid / kRedQuads;
-  f32x4 acc[G];
+  Partial st[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int h = 0; h < G; ++h) st[h] = Partial{kNegInf, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
   for (int p0 = pg; p0 < np; p0 += kRedGroups * U) {
     f32x4 v[G][U];
     float2 m[G][U];
@@ -493,7 +463,7 @@ __global__ __launch_bounds__(kRedThreads) void pa_reduce_kernel(DecodeArgs a) {
       const float* base = a.ws_acc + ws_acc_index(row0 + h, sl, MP, 0, D) + 4 * q4;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int pc = min(p0 + u * kRedGroups, np - 1);
+        const int pc = min(p0 + u * kRedGroups, np - 1);   // always a written record
         m[h][u] = ml0[h * MP + pc];
         v[h][u] = *reinterpret_cast<const f32x4*>(base + (size_t)pc * 16);
       }
@@ -502,35 +472,41 @@ __global__ __launch_bounds__(kRedThreads) void pa_reduce_kernel(DecodeArgs a) {
     for (int h = 0; h < G; ++h) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
+        // a record holds the partition's normalised output: weight sum l, weighted sum l*acc
         const bool ok = p0 + u * kRedGroups < np;
-        const float wgt = ok ? m[h][u].y * __builtin_amdgcn_exp2f(m[h][u].x - Mh[h]) : 0.f;
-        acc[h] += wgt * v[h][u];
+        combine_into(st[h], ok ? m[h][u].x : kNegInf, ok ? m[h][u].y : 0.f,
+                     ok ? m[h][u].y * v[h][u] : f32x4{0.f, 0.f, 0.f, 0.f});
       }
     }
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    // reduce over the 16 partition groups of this wave (lane bits 2..5)
+    // combine the 16 partition groups of this wave (lane bits 2..5)
 #pragma unroll
     for (int k = kRedQuads; k < 64; k <<= 1) {
+      const float om = __shfl_xor(st[h].m, k, 64);
+      const float ow = __shfl_xor(st[h].w, k, 64);
+      f32x4 oa;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[h][e] = xor_add(acc[h][e], k);
+      for (int e = 0; e < 4; ++e) oa[e] = __shfl_xor(st[h].a[e], k, 64);
+      combine_into(st[h], om, ow, oa);
     }
-    if (lane < kRedQuads) part_sum[wave][h][lane] = acc[h];
+    if (lane < kRedQuads) {
+      red_m[wave][h][lane] = st[h].m;
+      red_w[wave][h][lane] = st[h].w;
+      red_a[wave][h][lane] = st[h].a;
+    }
   }
   __syncthreads();
   if (tid < G * kRedQuads) {
     const int h = tid / kRedQuads, qq = tid % kRedQuads;
-    f32x4 t = part_sum[0][h][qq];
+    Partial t{red_m[0][h][qq], red_w[0][h][qq], red_a[0][h][qq]};
 #pragma unroll
-    for (int w = 1; w < kRedWaves; ++w) t += part_sum[w][h][qq];
-    float iw = inv_w[0];
-#pragma unroll
-    for (int hh = 1; hh < G; ++hh) iw = hh == h ? inv_w[hh] : iw;
-    t *= iw;
+    for (int w = 1; w < kRedWaves; ++w) combine_into(t, red_m[w][h][qq], red_w[w][h][qq], red_a[w][h][qq]);
+    const f32x4 y = t.a * (1.f / t.w);
     uint16_t* o = static_cast<uint16_t*>(a.out) + (row0 + h) * D + sl * kRedSlice + 4 * qq;
-    const u32x2 packed = {DT::bits(t[0]) | (DT::bits(t[1]) << 16),
-                          DT::bits(t[2]) | (DT::bits(t[3]) << 16)};
+    const u32x2 packed = {DT::bits(y[0]) | (DT::bits(y[1]) << 16),
+                          DT::bits(y[2]) | (DT::bits(y[3]) << 16)};
     *reinterpret_cast<u32x2*>(o) = packed;
   }
 }
