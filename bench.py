@@ -106,8 +106,8 @@ def main():
                     choices=["tiny", "batch", "long", "mixed", "saturation"])
     ap.add_argument("--partition-size", type=int, default=0,
                     help="tokens per partition; 0 = automatic (one workgroup per CU)")
-    ap.add_argument("--skip-p512", action="store_true",
-                    help="skip the extra timing at the pages' 512-token partitions")
+    ap.add_argument("--p512", action="store_true",
+                    help="also time the pages' fixed 512-token partitions (context only)")
     ap.add_argument("--single-pass-max-len", type=int, default=None)
     ap.add_argument("--cpu-seqs", type=int, default=4,
                     help="sequences of the workload the CPU oracle is timed on")
@@ -202,7 +202,7 @@ def main():
         f"median {ph1[len(ph1) // 2] * 1e3:.1f} us")
     # context: the pages' fixed 512-token partitions on the same inputs
     p512_ms = None
-    if P != 512 and not args.skip_p512:
+    if P != 512 and args.p512:
         d512 = decoder(512)
         for _ in range(args.warmup):
             step(d512)

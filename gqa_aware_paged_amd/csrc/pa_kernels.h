@@ -198,7 +198,7 @@ __device__ __forceinline__ float xor_add(float x, int m) { return x + __shfl_xor
 // Phase 1 (and the single-pass tier).
 // ---------------------------------------------------------------------------
 template <int D, class DT, int W>
-__global__ __launch_bounds__(W * 64, 2) void pa_phase1_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_kernel(DecodeArgs a) {
   constexpr int KS = D / 32;               // k-steps of the QK^T MFMA (32 dims each)
   constexpr int DB = D / 16;               // 16-wide head_dim blocks of the PV MFMA
   constexpr int LOADS = D / 32;            // 16-byte loads per lane per tile (K or V)

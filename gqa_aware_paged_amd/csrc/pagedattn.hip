@@ -22,7 +22,10 @@
 
 namespace {
 
-constexpr int kWaves = 4;                   // waves per phase-1 workgroup
+#ifndef PA_WAVES
+#define PA_WAVES 4
+#endif
+constexpr int kWaves = PA_WAVES;            // waves per phase-1 workgroup
 constexpr int kMinAutoPartition = 256;     // tokens: smallest automatic partition
 constexpr int kDefaultCUs = 256;            // MI355X
 constexpr float kLog2e = 1.4426950408889634f;
