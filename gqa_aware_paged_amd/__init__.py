@@ -36,7 +36,8 @@ class PlanInfo(ctypes.Structure):
                 ("phase2_workgroups", ctypes.c_longlong),
                 ("active_workgroups", ctypes.c_longlong), ("single_pass_seqs", ctypes.c_int),
                 ("partitioned_seqs", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t),
-                ("threads_per_workgroup", ctypes.c_int), ("lds_bytes_phase1", ctypes.c_int)]
+                ("threads_per_workgroup", ctypes.c_int), ("lds_bytes_phase1", ctypes.c_int),
+                ("balanced", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

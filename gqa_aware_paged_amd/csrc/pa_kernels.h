@@ -1,10 +1,10 @@
 // Device code of libpagedattn: GQA-grouped paged-attention decode for gfx950 (CDNA4).
 //
-// Phase 1 (pa_phase1_kernel): one workgroup per (sequence, KV head, partition).
-// The workgroup serves every query head of the KV head's group, so each K/V
-// page is fetched from HBM once (page of commit 8d26e23, "Key design change":
-// grid on KV heads instead of query heads).  Its W waves split the partition's
-// 16-token tiles; each wave
+// Phase 1 works on "pieces": a contiguous run of 16-token tiles of one
+// (sequence, KV head) segment.  One workgroup serves every query head of the
+// KV head's group, so each K/V page is fetched from HBM once (page of commit
+// 8d26e23, "Key design change": grid on KV heads instead of query heads).  Its W
+// waves split the piece's tiles; each wave
 //   1. gathers the tile through the block table with coalesced 16-byte global
 //      loads (one tile = one contiguous 16 x head_dim run of a page),
 //   2. stages it in its own XOR-swizzled LDS slot,
@@ -16,14 +16,23 @@
 //      never leaves registers.
 // The waves then merge their (max, sum, acc) states through LDS with the
 // flash-attention rescale, and the workgroup writes either the final output
-// (single-pass tier) or the partition's compound partial (page of commit
-// 8d26e23: max_score, exp_sum, weighted_v).
+// (the piece is the whole segment: single pass) or the piece's compound
+// partial (page of commit 8d26e23: max_score, exp_sum, weighted_v).
 //
-// Phase 2 (pa_reduce_kernel): one workgroup per (sequence, KV head, 16-wide
-// slice of head_dim) merges the partials of all partitions for the group's
-// query heads with the rescale of the online-softmax fix (page of commit
-// 87a19d2): with M the largest max, each partition weighs l_p 2^(m_p - M) and
-// out = sum_p weight_p acc_p / sum_p weight_p, evaluated as an associative fold.
+// Two ways of cutting the work into pieces:
+//  - pa_phase1_kernel: the pages' grid (sequence, KV head, partition) with a
+//    fixed partition size; a sequence no longer than the single-pass bound is
+//    one piece (page of commit b80fd2b, three-tier decode dispatch).
+//  - pa_phase1_balanced_kernel: the step's tiles, (sequence, KV head) segments
+//    laid end to end, are cut into one equal share per workgroup, computed on
+//    the device from seq_lens.  A segment inside one share is one pass; a
+//    segment crossing shares is partitioned at the share boundaries.  Every
+//    workgroup then streams the same number of bytes whatever the length mix.
+//
+// Phase 2 (pa_reduce_kernel) merges the partials of each partitioned segment
+// with the rescale of the online-softmax fix (page of commit 87a19d2): with M
+// the largest max, partial p weighs l_p 2^(m_p - M) and the output is
+// sum_p weight_p acc_p / sum_p weight_p, evaluated as an associative fold.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -84,6 +93,14 @@ struct BF16 {
 // ---------------------------------------------------------------------------
 // Kernel arguments (passed by value).
 // ---------------------------------------------------------------------------
+// Partial records.  A record holds, for each of the G query heads of one KV
+// head, the normalised output of a piece (fp32) and (max in base 2, exp sum).
+// ws_acc is [D/16][R][G][16] floats (slice-major: phase 2 reads the records of
+// one 16-wide slice back to back) and ws_ml is [R][G] float2.
+//  - grid mode:     record (s*Hkv + kvh)*max_parts + partition, R = S*Hkv*max_parts
+//  - balanced mode: record 2*w + slot of workgroup w (slot 0: the piece that
+//                   ends a segment begun earlier, slot 1: the piece that begins a
+//                   segment continued later), R = 2*num_wg
 struct DecodeArgs {
   void* out;
   const uint16_t* q;
@@ -91,8 +108,10 @@ struct DecodeArgs {
   const uint16_t* vc;
   const int32_t* bt;
   const int32_t* seq_lens;
-  float* ws_acc;            // [S][Hq][max_parts][D]
-  float2* ws_ml;            // [S][Hq][max_parts] (max in base 2, exp sum)
+  float* ws_acc;
+  float2* ws_ml;
+  int2* jobs;               // balanced mode: [num_wg] (segment, partial count) or (-1, 0)
+  long long records;        // R
   int num_seqs;
   int num_heads;
   int num_kv_heads;
@@ -100,9 +119,10 @@ struct DecodeArgs {
   int block_size;
   int max_blocks_per_seq;
   int max_seq_len;          // lengths are clamped to this bound
-  int partition_size;
-  int single_pass_max_len;
-  int max_parts;
+  int partition_size;       // grid mode
+  int single_pass_max_len;  // grid mode
+  int max_parts;            // grid mode
+  int num_wg;               // balanced mode: workgroups of phase 1
   float scale_log2;         // scale * log2(e)
 };
 
@@ -120,33 +140,15 @@ struct GatherArgs {
   int max_seq_len;
 };
 
-// Tokens [t_begin, t_end) one phase-1 workgroup covers; false if it has nothing to do.
-struct Span {
-  int t_begin, t_end;
-  bool single;
-};
+constexpr int kMaxBalancedSeqs = 1536;   // balanced mode keeps a prefix of seq_lens in LDS
 
-__device__ __forceinline__ bool workgroup_span(int L, int part, int P, int T1, Span& sp) {
-  sp.single = L <= T1;
-  if (sp.single) {
-    if (part != 0) return false;
-    sp.t_begin = 0;
-    sp.t_end = L > 0 ? L : 0;
-    return true;
-  }
-  const int np = (L + P - 1) / P;
-  if (part >= np) return false;
-  sp.t_begin = part * P;
-  sp.t_end = min(L, sp.t_begin + P);
-  return true;
+__device__ __forceinline__ size_t rec_acc_index(int slice, long long rec, int h, int G,
+                                                long long R) {
+  return ((static_cast<size_t>(slice) * R + rec) * G + h) * 16;
 }
 
-// Workspace layout of the normalised partition outputs: [S*Hq][D/16][max_parts][16]
-// floats, so the partitions of one 16-wide slice are contiguous (phase 2 reads
-// 1 KiB runs) and phase 1 writes 64-byte runs.
-__device__ __forceinline__ size_t ws_acc_index(size_t row, int c, int max_parts, int part,
-                                               int D) {
-  return ((row * (D / 16) + c) * max_parts + part) * 16;
+__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int s) {
+  return min(a.seq_lens[s], a.max_seq_len);
 }
 
 // Element offset of token t0 (a multiple of 16) of KV head kvh of sequence s.
@@ -195,45 +197,44 @@ __device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shf
 __device__ __forceinline__ float xor_add(float x, int m) { return x + __shfl_xor(x, m, 64); }
 
 // ---------------------------------------------------------------------------
-// Phase 1 (and the single-pass tier).
+// Phase 1: one piece = tokens [t_begin, t_end) of segment (s, kvh).
 // ---------------------------------------------------------------------------
+template <int D, int W>
+struct Phase1Lds {
+  static constexpr int kTileBytes = kTile * D * 2;
+  unsigned char tiles[W * 2 * kTileBytes];   // per wave: K tile, V tile; merge area at the end
+  unsigned char q[kTileBytes];               // the group's Q rows (16 rows, zero-padded)
+};
+
+// Runs one piece with the whole workgroup.  `final` writes the output rows of
+// the group; otherwise the piece's partial goes to record `rec`.  Starts with a
+// barrier, so LDS from a previous piece may be reused.
 template <int D, class DT, int W>
-__global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_kernel(DecodeArgs a) {
+__device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& sm, int s,
+                                          int kvh, int t_begin, int t_end, bool final,
+                                          long long rec) {
   constexpr int KS = D / 32;               // k-steps of the QK^T MFMA (32 dims each)
   constexpr int DB = D / 16;               // 16-wide head_dim blocks of the PV MFMA
   constexpr int LOADS = D / 32;            // 16-byte loads per lane per tile (K or V)
-  constexpr int TILE_BYTES = kTile * D * 2;
+  constexpr int TILE_BYTES = Phase1Lds<D, W>::kTileBytes;
   using Z = Swz<D>;
   static_assert((W - 1) * DB * 64 * 16 + 2 * (W - 1) * 64 * 4 <= W * 2 * TILE_BYTES,
                 "merge area must fit in the tile slots");
-  __shared__ __attribute__((aligned(16))) unsigned char lds[W * 2 * TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_q[TILE_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int Hkv = a.num_kv_heads;
   const int G = a.group;
   const int Hq = a.num_heads;
-
-  int wg = blockIdx.x;
-  const int kvh = wg % Hkv;
-  wg /= Hkv;
-  const int s = wg % a.num_seqs;
-  const int part = wg / a.num_seqs;
-
-  const int L = min(a.seq_lens[s], a.max_seq_len);
-  Span sp;
-  if (!workgroup_span(L, part, a.partition_size, a.single_pass_max_len, sp)) return;
-
   const int col = lane & 15;     // query head (QK^T/PV columns) or row index within a tile
   const int grp = lane >> 4;     // 4-lane-group index: k-slot block / 4-row block
 
   // the wave's first tile is requested before Q is staged, so the two latencies overlap
-  const int n_tiles = (sp.t_end - sp.t_begin + kTile - 1) / kTile;
+  const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
   u32x4 rk[LOADS], rv[LOADS];
   int it = wave;
   if (it < n_tiles) {
-    const size_t off = tile_offset(a.bt, s, sp.t_begin + kTile * it, kvh, Hkv, a.block_size,
+    const size_t off = tile_offset(a.bt, s, t_begin + kTile * it, kvh, Hkv, a.block_size,
                                    a.max_blocks_per_seq, D);
     load_tile<D>(a.kc + off, lane, rk);
     load_tile<D>(a.vc + off, lane, rv);
@@ -241,16 +242,17 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_kernel(DecodeArgs a) 
 
   // Q of the group, staged once in LDS as the B operand of S^T = K Q^T: row h is
   // query head kvh*G + h (rows G..15 are zero), swizzled like a K tile.
+  __syncthreads();
   {
     const uint16_t* qg = a.q + ((size_t)s * Hq + (size_t)kvh * G) * D;
     for (int i = threadIdx.x; i < kTile * Z::kChunks; i += W * 64) {
       const int row = i / Z::kChunks, c = i % Z::kChunks;
       u32x4 v = {0, 0, 0, 0};
       if (row < G) v = *reinterpret_cast<const u32x4*>(qg + row * D + 8 * c);
-      *reinterpret_cast<u32x4*>(lds_q + Z::byte_off(row, c)) = v;
+      *reinterpret_cast<u32x4*>(sm.q + Z::byte_off(row, c)) = v;
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   float m_run = kNegInf;          // running max of the head `col` (base-2 logits)
   float l_run = 0.f;              // this lane's share of the running exp sum
@@ -258,11 +260,11 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_kernel(DecodeArgs a) 
 #pragma unroll
   for (int c = 0; c < DB; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  unsigned char* ldsK = lds + wave * 2 * TILE_BYTES;
+  unsigned char* ldsK = sm.tiles + wave * 2 * TILE_BYTES;
   unsigned char* ldsV = ldsK + TILE_BYTES;
 
   for (; it < n_tiles; it += W) {
-    const int t0 = sp.t_begin + kTile * it;
+    const int t0 = t_begin + kTile * it;
     // stage the tile in this wave's LDS slot
     wave_lds_fence();
 #pragma unroll
@@ -288,7 +290,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_kernel(DecodeArgs a) 
     for (int ks = 0; ks < KS; ++ks) {
       const int off = Z::byte_off(col, 4 * ks + grp);
       const u32x4 kop = *reinterpret_cast<const u32x4*>(ldsK + off);
-      const u32x4 qop = *reinterpret_cast<const u32x4*>(lds_q + off);
+      const u32x4 qop = *reinterpret_cast<const u32x4*>(sm.q + off);
       st = DT::mfma_qk(kop, qop, st);
     }
 
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_kernel(DecodeArgs a) 
     const int tk = t0 + 4 * grp;
     float x[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = (tk + e < sp.t_end) ? st[e] * a.scale_log2 : kNegInf;
+    for (int e = 0; e < 4; ++e) x[e] = (tk + e < t_end) ? st[e] * a.scale_log2 : kNegInf;
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = xor_max(mx, 16);
     mx = xor_max(mx, 32);
@@ -318,10 +320,10 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_kernel(DecodeArgs a) 
     // row-major tile: within each 16-lane group, result lane i, element j comes
     // from source lane i/4 + 4j, element i%4, so source lane r addresses row
     // 4*grp + r/4, columns 16c + 4*(r%4) .. +3.
-    const bool tail = t0 + kTile > sp.t_end;
+    const bool tail = t0 + kTile > t_end;
     uint32_t keep_lo = 0xffffffffu, keep_hi = 0xffffffffu;   // masks slots past the end
     if (tail) {
-      const int n = sp.t_end - tk;                              // valid tokens of this lane
+      const int n = t_end - tk;                                 // valid tokens of this lane
       keep_lo = (n > 0 ? 0x0000ffffu : 0u) | (n > 1 ? 0xffff0000u : 0u);
       keep_hi = (n > 2 ? 0x0000ffffu : 0u) | (n > 3 ? 0xffff0000u : 0u);
     }
@@ -345,9 +347,9 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_kernel(DecodeArgs a) 
 
   // merge the W wave states: waves 1..W-1 park (acc, m, l) in LDS, wave 0 combines
   __syncthreads();
-  f32x4* park = reinterpret_cast<f32x4*>(lds);                     // [W-1][DB][64]
+  f32x4* park = reinterpret_cast<f32x4*>(sm.tiles);                    // [W-1][DB][64]
   float* park_m = reinterpret_cast<float*>(park + (W - 1) * DB * 64);  // [W-1][64]
-  float* park_l = park_m + (W - 1) * 64;                           // [W-1][64]
+  float* park_l = park_m + (W - 1) * 64;                               // [W-1][64]
   if (wave > 0) {
 #pragma unroll
     for (int c = 0; c < DB; ++c) park[((wave - 1) * DB + c) * 64 + lane] = acc[c];
@@ -355,54 +357,178 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_kernel(DecodeArgs a) 
     park_l[(wave - 1) * 64 + lane] = l_run;
   }
   __syncthreads();
-  if (wave != 0) return;
-
-  float M = m_run;
+  if (wave == 0) {
+    float M = m_run;
 #pragma unroll
-  for (int w = 1; w < W; ++w) M = fmaxf(M, park_m[(w - 1) * 64 + lane]);
-  const bool empty = M == kNegInf;   // no token at all (seq_len <= 0)
-  float f = empty ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-  float Lsum = f * l_run;
+    for (int w = 1; w < W; ++w) M = fmaxf(M, park_m[(w - 1) * 64 + lane]);
+    const bool empty = M == kNegInf;   // no token at all (seq_len <= 0)
+    const float f = empty ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+    float Lsum = f * l_run;
 #pragma unroll
-  for (int c = 0; c < DB; ++c) acc[c] *= f;
+    for (int c = 0; c < DB; ++c) acc[c] *= f;
 #pragma unroll
-  for (int w = 1; w < W; ++w) {
-    const float mw = park_m[(w - 1) * 64 + lane];
-    const float fw = empty ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-    Lsum += fw * park_l[(w - 1) * 64 + lane];
+    for (int w = 1; w < W; ++w) {
+      const float mw = park_m[(w - 1) * 64 + lane];
+      const float fw = empty ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      Lsum += fw * park_l[(w - 1) * 64 + lane];
 #pragma unroll
-    for (int c = 0; c < DB; ++c) acc[c] += fw * park[((w - 1) * DB + c) * 64 + lane];
-  }
-  if (col >= G) return;
-  const int hq = kvh * G + col;
-  const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-  if (sp.single) {
-    uint16_t* o = static_cast<uint16_t*>(a.out) + ((size_t)s * Hq + hq) * D + 4 * grp;
-#pragma unroll
-    for (int c = 0; c < DB; ++c) {
-      const f32x4 y = acc[c] * inv;
-      const u32x2 packed = {DT::bits(y[0]) | (DT::bits(y[1]) << 16),
-                            DT::bits(y[2]) | (DT::bits(y[3]) << 16)};
-      *reinterpret_cast<u32x2*>(o + 16 * c) = packed;
+      for (int c = 0; c < DB; ++c) acc[c] += fw * park[((w - 1) * DB + c) * 64 + lane];
     }
-  } else {
-    const size_t row = (size_t)s * Hq + hq;
+    if (col < G) {
+      const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+      if (final) {
+        uint16_t* o = static_cast<uint16_t*>(a.out) + ((size_t)s * Hq + kvh * G + col) * D +
+                      4 * grp;
 #pragma unroll
-    for (int c = 0; c < DB; ++c)
-      *reinterpret_cast<f32x4*>(a.ws_acc + ws_acc_index(row, c, a.max_parts, part, D) +
-                                4 * grp) = acc[c] * inv;
-    if (grp == 0) a.ws_ml[row * a.max_parts + part] = make_float2(M, Lsum);
+        for (int c = 0; c < DB; ++c) {
+          const f32x4 y = acc[c] * inv;
+          const u32x2 packed = {DT::bits(y[0]) | (DT::bits(y[1]) << 16),
+                                DT::bits(y[2]) | (DT::bits(y[3]) << 16)};
+          *reinterpret_cast<u32x2*>(o + 16 * c) = packed;
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < DB; ++c)
+          *reinterpret_cast<f32x4*>(a.ws_acc + rec_acc_index(c, rec, col, G, a.records) +
+                                    4 * grp) = acc[c] * inv;
+        if (grp == 0) a.ws_ml[rec * G + col] = make_float2(M, Lsum);
+      }
+    }
   }
 }
 
+// Grid mode: workgroup (partition, sequence, KV head), partition slowest.
+template <int D, class DT, int W>
+__global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) Phase1Lds<D, W> sm;
+  int wg = blockIdx.x;
+  const int kvh = wg % a.num_kv_heads;
+  wg /= a.num_kv_heads;
+  const int s = wg % a.num_seqs;
+  const int part = wg / a.num_seqs;
+  const int L = clamp_len(a, s);
+  const bool single = L <= a.single_pass_max_len;
+  int t_begin, t_end;
+  if (single) {
+    if (part != 0) return;
+    t_begin = 0;
+    t_end = L > 0 ? L : 0;
+  } else {
+    const int np = (L + a.partition_size - 1) / a.partition_size;
+    if (part >= np) return;
+    t_begin = part * a.partition_size;
+    t_end = min(L, t_begin + a.partition_size);
+  }
+  const long long rec = ((long long)s * a.num_kv_heads + kvh) * a.max_parts + part;
+  run_piece<D, DT, W>(a, sm, s, kvh, t_begin, t_end, single, rec);
+}
+
+// Balanced mode.  Segment q = s*Hkv + kvh has n(s) = ceil(L_s/16) tiles; segments
+// are laid end to end (q order) into T tiles, and workgroup w takes tiles
+// [T*w/NW, T*(w+1)/NW).  Each workgroup rebuilds the per-sequence prefix of
+// tiles in LDS from seq_lens (S <= kMaxBalancedSeqs), then walks its share.
+template <int D, class DT, int W>
+__global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(DecodeArgs a) {
+  constexpr int NT = W * 64;
+  constexpr int PER = kMaxBalancedSeqs / NT;
+  __shared__ __attribute__((aligned(16))) Phase1Lds<D, W> sm;
+  __shared__ int pre[kMaxBalancedSeqs + 1];     // pre[s] = tiles of sequences < s (one KV head)
+  __shared__ int wave_tot[W];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int S = a.num_seqs, Hkv = a.num_kv_heads;
+  const int w = blockIdx.x, NW = a.num_wg;
+
+  // ---- inclusive scan of tiles per sequence: thread tid owns sequences tid*PER ..
+  int local[PER];
+  int tsum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int s = tid * PER + i;
+    int n = 0;
+    if (s < S) {
+      const int L = clamp_len(a, s);
+      n = L > 0 ? (L + kTile - 1) / kTile : 0;
+    }
+    tsum += n;
+    local[i] = tsum;
+  }
+  int incl = tsum;
+#pragma unroll
+  for (int k = 1; k < 64; k <<= 1) {
+    const int v = __shfl_up(incl, k, 64);
+    if (lane >= k) incl += v;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int base = incl - tsum;
+  for (int v = 0; v < wave; ++v) base += wave_tot[v];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int s = tid * PER + i;
+    if (s < S) pre[s + 1] = base + local[i];
+  }
+  if (tid == 0) pre[0] = 0;
+  __syncthreads();
+
+  const long long T = (long long)Hkv * pre[S];
+  const long long lo = T * w / NW, hi = T * (w + 1) / NW;
+
+  // sequences of length <= 0 get zero rows; spread over the workgroups
+  for (int s = w; s < S; s += NW) {
+    if (pre[s + 1] == pre[s]) {
+      uint16_t* o = static_cast<uint16_t*>(a.out) + (size_t)s * a.num_heads * D;
+      for (int i = tid; i < a.num_heads * D / 8; i += NT)
+        reinterpret_cast<u32x4*>(o)[i] = u32x4{0, 0, 0, 0};
+    }
+  }
+
+  int2 job = make_int2(-1, 0);
+  if (lo == hi) {
+    // an empty share (fewer tiles than workgroups) may lie inside a segment that
+    // neighbouring workgroups split: leave the identity (-inf, 0) in slot 0
+    for (int h = tid; h < a.group; h += NT)
+      a.ws_ml[2LL * w * a.group + h] = make_float2(kNegInf, 0.f);
+  } else {
+    // the sequence holding tile lo: largest s with Hkv*pre[s] <= lo (it has tiles)
+    int s = 0, top = S - 1;
+    while (s < top) {
+      const int mid = (s + top + 1) >> 1;
+      if ((long long)Hkv * pre[mid] <= lo) s = mid; else top = mid - 1;
+    }
+    long long x = lo;
+    while (x < hi) {
+      const int n = pre[s + 1] - pre[s];
+      const long long seq0 = (long long)Hkv * pre[s];
+      const int kvh = (int)((x - seq0) / n);
+      const long long seg0 = seq0 + (long long)kvh * n, seg1 = seg0 + n;
+      const int ta = (int)(x - seg0);
+      const int tb = (int)(min(hi, seg1) - seg0);
+      const bool final = ta == 0 && tb == n;
+      const long long rec = 2LL * w + (ta > 0 ? 0 : 1);
+      if (ta == 0 && !final) {
+        // this workgroup starts a segment that later ones continue: it owns the merge
+        const long long last = (seg1 * NW - 1) / T;      // workgroup holding tile seg1-1
+        job = make_int2(s * Hkv + kvh, (int)(last - w + 1));
+      }
+      const int L = clamp_len(a, s);
+      run_piece<D, DT, W>(a, sm, s, kvh, kTile * ta, min(L, kTile * tb), final, rec);
+      x = seg1 < hi ? seg1 : hi;
+      if (kvh + 1 == Hkv) {
+        do { ++s; } while (s < S && pre[s + 1] == pre[s] && x < hi);
+      }
+    }
+  }
+  if (tid == 0) a.jobs[w] = job;
+}
+
 // ---------------------------------------------------------------------------
-// Phase 2: merge the partitions of every partitioned sequence.
+// Phase 2: merge the partials of every partitioned segment.
 // ---------------------------------------------------------------------------
-constexpr int kRedSlice = 16;                 // head_dim values per workgroup (one d-block)
-constexpr int kRedQuads = kRedSlice / 4;      // float4 lanes per slice (fastest in a wave)
 constexpr int kRedThreads = 256;
 constexpr int kRedWaves = kRedThreads / 64;
-constexpr int kRedGroups = kRedThreads / kRedQuads;   // partition groups (64)
 
 // Merge of two compound partials (m, w, a): m is a base-2 max, w the weight sum
 // and a the weighted sum, both relative to m.  (-inf, 0, 0) is the identity.
@@ -420,60 +546,82 @@ __device__ __forceinline__ void combine_into(Partial& x, float om, float ow, f32
   x.m = nm;
 }
 
-// Workgroup (s, kvh, slice) merges the partitions of the G query heads of KV head
-// kvh for head_dim values [16*slice, +16).  Thread (pg, q4) folds partitions
-// p = pg + 64k of every head into a running partial (the rescale rule of the
-// online-softmax fix), issuing all loads of a round (G heads x U partitions)
-// before consuming any; the 64 partition groups are then combined with the same
-// rule by lane shuffles (16 groups per wave) and through LDS (4 waves).  G is a
-// template parameter so the per-head state lives in registers.
-template <int D, class DT, int G>
+// Workgroup = (segment, SPW consecutive 16-wide head_dim slices).  Thread
+// (pg, ql) covers head_dim values 4*ql .. +3 of the workgroup's slices and folds
+// partials p = pg, pg + PG, ... of every head into a running partial, issuing all
+// loads of a round (G heads x U partials) before consuming any; the PG groups are
+// then combined with the same rule by lane shuffles and through LDS.
+//   grid mode (BAL = false): workgroup (segment q, slice group), partials
+//     q*max_parts + p for p < ceil(L/P); segments in one pass are skipped.
+//   balanced mode (BAL = true): workgroup (w, slice group) merges the segment
+//     begun by phase-1 workgroup w, if any: record 2w+1, then 2(w+p) for p >= 1.
+template <int D, class DT, int G, int SPW, bool BAL>
 __global__ __launch_bounds__(kRedThreads) void pa_reduce_kernel(DecodeArgs a) {
-  constexpr int NSL = D / kRedSlice;
+  constexpr int NSG = D / 16 / SPW;        // slice groups per segment
+  constexpr int QL = 4 * SPW;              // float4 lanes per partial group
+  constexpr int PG = kRedThreads / QL;     // partial groups
   constexpr int U = G >= 16 ? 1 : (G >= 6 ? 2 : (G >= 3 ? 4 : 8));
-  __shared__ float red_m[kRedWaves][G][kRedQuads], red_w[kRedWaves][G][kRedQuads];
-  __shared__ f32x4 red_a[kRedWaves][G][kRedQuads];
+  static_assert(QL <= 64, "a partial group must fit in a wave");
+  __shared__ float red_m[kRedWaves][G][QL], red_w[kRedWaves][G][QL];
+  __shared__ f32x4 red_a[kRedWaves][G][QL];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int Hkv = a.num_kv_heads, Hq = a.num_heads, MP = a.max_parts;
-  int wg = blockIdx.x;
-  const int sl = wg % NSL;
-  wg /= NSL;
-  const int kvh = wg % Hkv;
-  const int s = wg / Hkv;
+  const int Hkv = a.num_kv_heads, Hq = a.num_heads;
+  const int sg = blockIdx.x % NSG;
+  const int unit = blockIdx.x / NSG;
 
-  const int L = min(a.seq_lens[s], a.max_seq_len);
-  if (L <= a.single_pass_max_len) return;       // served in one pass by phase 1
-  const int np = (L + a.partition_size - 1) / a.partition_size;
-  const size_t row0 = (size_t)s * Hq + (size_t)kvh * G;   // first query head of the group
-  const float2* ml0 = a.ws_ml + row0 * MP;
+  int q, np;
+  long long rec0, step, first;
+  if constexpr (BAL) {
+    const int2 job = a.jobs[unit];
+    if (job.x < 0) return;
+    q = job.x;
+    np = job.y;
+    rec0 = 2LL * unit;
+    step = 2;
+    first = 1;
+  } else {
+    q = unit;
+    const int L = clamp_len(a, q / Hkv);
+    if (L <= a.single_pass_max_len) return;     // served in one pass by phase 1
+    np = (L + a.partition_size - 1) / a.partition_size;
+    rec0 = (long long)q * a.max_parts;
+    step = 1;
+    first = 0;
+  }
+  const int s = q / Hkv, kvh = q % Hkv;
+  const long long R = a.records;
 
-  const int q4 = tid % kRedQuads;
-  const int pg = tid / kRedQuads;
+  const int ql = tid % QL;
+  const int pg = tid / QL;
+  const int slice = sg * SPW + ql / 4;
+  const int q4 = ql % 4;
   Partial st[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) st[h] = Partial{kNegInf, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
-  for (int p0 = pg; p0 < np; p0 += kRedGroups * U) {
+  for (int p0 = pg; p0 < np; p0 += PG * U) {
     f32x4 v[G][U];
     float2 m[G][U];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float* base = a.ws_acc + ws_acc_index(row0 + h, sl, MP, 0, D) + 4 * q4;
+    for (int u = 0; u < U; ++u) {
+      const int pc = min(p0 + u * PG, np - 1);           // always a written record
+      const long long rec = rec0 + step * pc + (pc == 0 ? first : 0);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int pc = min(p0 + u * kRedGroups, np - 1);   // always a written record
-        m[h][u] = ml0[h * MP + pc];
-        v[h][u] = *reinterpret_cast<const f32x4*>(base + (size_t)pc * 16);
+      for (int h = 0; h < G; ++h) {
+        m[h][u] = a.ws_ml[rec * G + h];
+        v[h][u] = *reinterpret_cast<const f32x4*>(a.ws_acc + rec_acc_index(slice, rec, h, G, R) +
+                                                  4 * q4);
       }
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        // a record holds the partition's normalised output: weight sum l, weighted sum l*acc
-        const bool ok = p0 + u * kRedGroups < np;
+        // a record holds the piece's normalised output: weight sum l, weighted sum l*acc;
+        // a max of -inf marks the identity (an empty share in balanced mode)
+        const bool ok = p0 + u * PG < np && m[h][u].x != kNegInf;
         combine_into(st[h], ok ? m[h][u].x : kNegInf, ok ? m[h][u].y : 0.f,
                      ok ? m[h][u].y * v[h][u] : f32x4{0.f, 0.f, 0.f, 0.f});
       }
@@ -481,9 +629,9 @@ __global__ __launch_bounds__(kRedThreads) void pa_reduce_kernel(DecodeArgs a) {
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    // combine the 16 partition groups of this wave (lane bits 2..5)
+    // combine the partial groups of this wave (lane bits log2(QL) .. 5)
 #pragma unroll
-    for (int k = kRedQuads; k < 64; k <<= 1) {
+    for (int k = QL; k < 64; k <<= 1) {
       const float om = __shfl_xor(st[h].m, k, 64);
       const float ow = __shfl_xor(st[h].w, k, 64);
       f32x4 oa;
@@ -491,20 +639,21 @@ __global__ __launch_bounds__(kRedThreads) void pa_reduce_kernel(DecodeArgs a) {
       for (int e = 0; e < 4; ++e) oa[e] = __shfl_xor(st[h].a[e], k, 64);
       combine_into(st[h], om, ow, oa);
     }
-    if (lane < kRedQuads) {
+    if (lane < QL) {
       red_m[wave][h][lane] = st[h].m;
       red_w[wave][h][lane] = st[h].w;
       red_a[wave][h][lane] = st[h].a;
     }
   }
   __syncthreads();
-  if (tid < G * kRedQuads) {
-    const int h = tid / kRedQuads, qq = tid % kRedQuads;
+  for (int i = tid; i < G * QL; i += kRedThreads) {
+    const int h = i / QL, qq = i % QL;
     Partial t{red_m[0][h][qq], red_w[0][h][qq], red_a[0][h][qq]};
 #pragma unroll
     for (int w = 1; w < kRedWaves; ++w) combine_into(t, red_m[w][h][qq], red_w[w][h][qq], red_a[w][h][qq]);
     const f32x4 y = t.a * (1.f / t.w);
-    uint16_t* o = static_cast<uint16_t*>(a.out) + (row0 + h) * D + sl * kRedSlice + 4 * qq;
+    uint16_t* o = static_cast<uint16_t*>(a.out) + ((size_t)s * Hq + kvh * G + h) * D +
+                  sg * SPW * 16 + 4 * qq;
     const u32x2 packed = {DT::bits(y[0]) | (DT::bits(y[1]) << 16),
                           DT::bits(y[2]) | (DT::bits(y[3]) << 16)};
     *reinterpret_cast<u32x2*>(o) = packed;

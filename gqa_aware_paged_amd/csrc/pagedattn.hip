@@ -30,14 +30,20 @@ constexpr int kMinAutoPartition = 256;     // tokens: smallest automatic partiti
 constexpr int kDefaultCUs = 256;            // MI355X
 constexpr float kLog2e = 1.4426950408889634f;
 
+constexpr int kMinTilesPerWG = 16;        // balanced mode: at least 4 tiles per wave
+constexpr int kBalancedSlices = 4;        // balanced phase 2: 16-wide slices per workgroup
+
 struct Plan {
-  int P = 0;             // partition size (tokens)
-  int T1 = 0;            // single-pass threshold (tokens)
-  int max_parts = 0;     // partitions per (seq, kv head) slot; 0 = no phase 2
+  bool balanced = false; // length-balanced split (partition_size 0) vs fixed partitions
+  int P = 0;             // partition size (tokens), grid mode
+  int T1 = 0;            // single-pass threshold (tokens), grid mode
+  int max_parts = 0;     // partitions per (seq, kv head) slot; 0 = no phase 2, grid mode
   int max_seq_len = 0;   // resolved length bound
   int group = 0;
+  int num_wg = 0;        // phase-1 workgroups, balanced mode
+  long long records = 0; // partial records in the workspace
   long long grid1 = 0, grid2 = 0;
-  size_t ws_acc_bytes = 0, ws_bytes = 0;
+  size_t ws_ml_off = 0, ws_jobs_off = 0, ws_bytes = 0;
 };
 
 bool supported_head_dim(int d) { return d == 128 || d == 256; }
@@ -58,9 +64,11 @@ int check_sizes(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, in
   return PA_OK;
 }
 
-// Partition size when the caller passes 0: spread the step's K/V over one
-// workgroup per compute unit.  The work estimate is num_seqs * max_seq_len tokens
-// per KV head (exact for equal lengths), or the caller's total-token hint.
+// Fixed partition size when the caller passes 0 but the balanced split does not
+// apply (a forced tier, or more sequences than it keeps in LDS): spread the
+// step's K/V over one workgroup per compute unit.  The work estimate is
+// num_seqs * max_seq_len tokens per KV head (exact for equal lengths), or the
+// caller's total-token hint.
 int auto_partition(long long S, int Hkv, int max_len, int cus, long long total_hint) {
   const long long tokens = total_hint > 0 ? total_hint : S * max_len;
   long long p = (tokens * Hkv + cus - 1) / cus;
@@ -71,26 +79,48 @@ int auto_partition(long long S, int Hkv, int max_len, int cus, long long total_h
   return static_cast<int>(p);
 }
 
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
 int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int P_req,
               const pa_options* opt, Plan& pl) {
   pl = Plan{};
   pl.group = Hq / Hkv;
   pl.max_seq_len = max_len > 0 ? max_len : mbps * bs;
   const int cus = (opt && opt->num_cus > 0) ? opt->num_cus : kDefaultCUs;
-  const long long hint = opt ? opt->total_tokens_hint : 0;
-  pl.P = P_req > 0 ? P_req : auto_partition(S, Hkv, pl.max_seq_len, cus, hint);
-  // a sequence that fits in one partition is served in one pass
-  pl.T1 = (opt && opt->single_pass_max_len >= 0) ? opt->single_pass_max_len : pl.P;
-  if (pl.max_seq_len > pl.T1) pl.max_parts = (pl.max_seq_len + pl.P - 1) / pl.P;
-  const long long parts = pl.max_parts > 0 ? pl.max_parts : 1;
-  pl.grid1 = static_cast<long long>(S) * Hkv * parts;
-  pl.grid2 = pl.max_parts > 0 ? static_cast<long long>(S) * Hkv * (D / pa::kRedSlice) : 0;
+  const bool forced_tier = opt && opt->single_pass_max_len >= 0;
+  pl.balanced = P_req == 0 && !forced_tier && S <= pa::kMaxBalancedSeqs;
+  if (pl.balanced) {
+    // two resident workgroups per CU, but at least kMinTilesPerWG tiles each
+    const long long tiles = static_cast<long long>(S) * Hkv * ((pl.max_seq_len + 15) / 16);
+    long long nw = (tiles + kMinTilesPerWG - 1) / kMinTilesPerWG;
+    if (nw > 2LL * cus) nw = 2LL * cus;
+    if (nw < 1) nw = 1;
+    pl.num_wg = static_cast<int>(nw);
+    pl.records = 2LL * pl.num_wg;
+    pl.grid1 = pl.num_wg;
+    pl.grid2 = static_cast<long long>(pl.num_wg) * (D / 16 / kBalancedSlices);
+    pl.T1 = -1;
+  } else {
+    const long long hint = opt ? opt->total_tokens_hint : 0;
+    pl.P = P_req > 0 ? P_req : auto_partition(S, Hkv, pl.max_seq_len, cus, hint);
+    // a sequence that fits in one partition is served in one pass
+    pl.T1 = forced_tier ? opt->single_pass_max_len : pl.P;
+    if (pl.max_seq_len > pl.T1) pl.max_parts = (pl.max_seq_len + pl.P - 1) / pl.P;
+    const long long parts = pl.max_parts > 0 ? pl.max_parts : 1;
+    pl.grid1 = static_cast<long long>(S) * Hkv * parts;
+    pl.grid2 = pl.max_parts > 0 ? static_cast<long long>(S) * Hkv * (D / 16) : 0;
+    pl.records = static_cast<long long>(S) * Hkv * pl.max_parts;
+  }
   if (pl.grid1 > std::numeric_limits<int>::max() || pl.grid2 > std::numeric_limits<int>::max())
     return PA_ERR_SHAPE;
-  if (pl.max_parts > 0) {
-    const size_t recs = static_cast<size_t>(S) * Hq * pl.max_parts;
-    pl.ws_acc_bytes = (recs * D * sizeof(float) + 255) & ~static_cast<size_t>(255);
-    pl.ws_bytes = pl.ws_acc_bytes + recs * sizeof(float2);
+  if (pl.records > 0) {
+    const size_t recs = static_cast<size_t>(pl.records) * pl.group;   // (record, head) pairs
+    pl.ws_ml_off = align256(recs * D * sizeof(float));
+    pl.ws_bytes = pl.ws_ml_off + recs * sizeof(float2);
+    if (pl.balanced) {
+      pl.ws_jobs_off = align256(pl.ws_bytes);
+      pl.ws_bytes = pl.ws_jobs_off + static_cast<size_t>(pl.num_wg) * sizeof(int2);
+    }
   }
   return PA_OK;
 }
@@ -99,30 +129,36 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 // Phase 2 is instantiated per group size so its loads can all be in flight at once.
 template <int D, class DT, int G>
-void launch_reduce_g(unsigned grid, hipStream_t stream, const pa::DecodeArgs& args) {
-  hipLaunchKernelGGL((pa::pa_reduce_kernel<D, DT, G>), dim3(grid), dim3(pa::kRedThreads), 0,
-                     stream, args);
+void launch_reduce_g(bool balanced, unsigned grid, hipStream_t stream,
+                     const pa::DecodeArgs& args) {
+  if (balanced)
+    hipLaunchKernelGGL((pa::pa_reduce_kernel<D, DT, G, kBalancedSlices, true>), dim3(grid),
+                       dim3(pa::kRedThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL((pa::pa_reduce_kernel<D, DT, G, 1, false>), dim3(grid),
+                       dim3(pa::kRedThreads), 0, stream, args);
 }
 
 template <int D, class DT>
-int launch_reduce(int group, unsigned grid, hipStream_t stream, const pa::DecodeArgs& args) {
+int launch_reduce(int group, bool balanced, unsigned grid, hipStream_t stream,
+                  const pa::DecodeArgs& args) {
   switch (group) {
-    case 1: launch_reduce_g<D, DT, 1>(grid, stream, args); break;
-    case 2: launch_reduce_g<D, DT, 2>(grid, stream, args); break;
-    case 3: launch_reduce_g<D, DT, 3>(grid, stream, args); break;
-    case 4: launch_reduce_g<D, DT, 4>(grid, stream, args); break;
-    case 5: launch_reduce_g<D, DT, 5>(grid, stream, args); break;
-    case 6: launch_reduce_g<D, DT, 6>(grid, stream, args); break;
-    case 7: launch_reduce_g<D, DT, 7>(grid, stream, args); break;
-    case 8: launch_reduce_g<D, DT, 8>(grid, stream, args); break;
-    case 9: launch_reduce_g<D, DT, 9>(grid, stream, args); break;
-    case 10: launch_reduce_g<D, DT, 10>(grid, stream, args); break;
-    case 11: launch_reduce_g<D, DT, 11>(grid, stream, args); break;
-    case 12: launch_reduce_g<D, DT, 12>(grid, stream, args); break;
-    case 13: launch_reduce_g<D, DT, 13>(grid, stream, args); break;
-    case 14: launch_reduce_g<D, DT, 14>(grid, stream, args); break;
-    case 15: launch_reduce_g<D, DT, 15>(grid, stream, args); break;
-    case 16: launch_reduce_g<D, DT, 16>(grid, stream, args); break;
+    case 1: launch_reduce_g<D, DT, 1>(balanced, grid, stream, args); break;
+    case 2: launch_reduce_g<D, DT, 2>(balanced, grid, stream, args); break;
+    case 3: launch_reduce_g<D, DT, 3>(balanced, grid, stream, args); break;
+    case 4: launch_reduce_g<D, DT, 4>(balanced, grid, stream, args); break;
+    case 5: launch_reduce_g<D, DT, 5>(balanced, grid, stream, args); break;
+    case 6: launch_reduce_g<D, DT, 6>(balanced, grid, stream, args); break;
+    case 7: launch_reduce_g<D, DT, 7>(balanced, grid, stream, args); break;
+    case 8: launch_reduce_g<D, DT, 8>(balanced, grid, stream, args); break;
+    case 9: launch_reduce_g<D, DT, 9>(balanced, grid, stream, args); break;
+    case 10: launch_reduce_g<D, DT, 10>(balanced, grid, stream, args); break;
+    case 11: launch_reduce_g<D, DT, 11>(balanced, grid, stream, args); break;
+    case 12: launch_reduce_g<D, DT, 12>(balanced, grid, stream, args); break;
+    case 13: launch_reduce_g<D, DT, 13>(balanced, grid, stream, args); break;
+    case 14: launch_reduce_g<D, DT, 14>(balanced, grid, stream, args); break;
+    case 15: launch_reduce_g<D, DT, 15>(balanced, grid, stream, args); break;
+    case 16: launch_reduce_g<D, DT, 16>(balanced, grid, stream, args); break;
     default: return PA_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -134,14 +170,19 @@ int launch_decode(const pa::DecodeArgs& args, const Plan& pl, hipStream_t stream
   if (opt && opt->phase1_begin) {
     if (hipEventRecord(opt->phase1_begin, stream) != hipSuccess) return PA_ERR_HIP;
   }
-  hipLaunchKernelGGL((pa::pa_phase1_kernel<D, DT, kWaves>), dim3(static_cast<unsigned>(pl.grid1)),
-                     dim3(kWaves * 64), 0, stream, args);
+  if (pl.balanced)
+    hipLaunchKernelGGL((pa::pa_phase1_balanced_kernel<D, DT, kWaves>),
+                       dim3(static_cast<unsigned>(pl.grid1)), dim3(kWaves * 64), 0, stream, args);
+  else
+    hipLaunchKernelGGL((pa::pa_phase1_kernel<D, DT, kWaves>),
+                       dim3(static_cast<unsigned>(pl.grid1)), dim3(kWaves * 64), 0, stream, args);
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   if (opt && opt->phase1_end) {
     if (hipEventRecord(opt->phase1_end, stream) != hipSuccess) return PA_ERR_HIP;
   }
   if (pl.grid2 > 0) {
-    const int st = launch_reduce<D, DT>(pl.group, static_cast<unsigned>(pl.grid2), stream, args);
+    const int st = launch_reduce<D, DT>(pl.group, pl.balanced, static_cast<unsigned>(pl.grid2),
+                                        stream, args);
     if (st != PA_OK) return st;
   }
   return PA_OK;
@@ -208,16 +249,43 @@ PA_API int paged_attn_plan(const int32_t* seq_lens_host, int num_seqs, int num_h
   info->workspace_bytes = pl.ws_bytes;
   info->threads_per_workgroup = kWaves * 64;
   info->lds_bytes_phase1 = kWaves * 2 * pa::kTile * head_dim * 2;
+  info->balanced = pl.balanced ? 1 : 0;
   if (seq_lens_host) {
-    for (int s = 0; s < num_seqs; ++s) {
-      int L = seq_lens_host[s] < pl.max_seq_len ? seq_lens_host[s] : pl.max_seq_len;
-      if (L <= pl.T1) {
-        info->single_pass_seqs++;
-        info->active_workgroups += num_kv_heads;
-      } else {
-        info->partitioned_seqs++;
-        info->active_workgroups += static_cast<long long>(num_kv_heads) *
-                                   ((L + pl.P - 1) / pl.P);
+    if (pl.balanced) {
+      // host mirror of the device split: segment q = s*Hkv + kvh covers tiles
+      // [start, start + n) of T; workgroup w takes [T*w/NW, T*(w+1)/NW)
+      long long T = 0;
+      for (int s = 0; s < num_seqs; ++s) {
+        const int L = seq_lens_host[s] < pl.max_seq_len ? seq_lens_host[s] : pl.max_seq_len;
+        T += static_cast<long long>(num_kv_heads) * (L > 0 ? (L + 15) / 16 : 0);
+      }
+      const long long NW = pl.num_wg;
+      long long start = 0;
+      for (int s = 0; s < num_seqs; ++s) {
+        const int L = seq_lens_host[s] < pl.max_seq_len ? seq_lens_host[s] : pl.max_seq_len;
+        const long long n = L > 0 ? (L + 15) / 16 : 0;
+        bool split = false;
+        for (int kvh = 0; kvh < num_kv_heads && n > 0; ++kvh, start += n) {
+          const long long first = ((start + 1) * NW - 1) / T;
+          const long long last = ((start + n) * NW - 1) / T;
+          split = split || first != last;
+        }
+        if (split) info->partitioned_seqs++;
+        else info->single_pass_seqs++;
+      }
+      for (long long w = 0; w < NW; ++w)
+        if (T * w / NW < T * (w + 1) / NW) info->active_workgroups++;
+    } else {
+      for (int s = 0; s < num_seqs; ++s) {
+        const int L = seq_lens_host[s] < pl.max_seq_len ? seq_lens_host[s] : pl.max_seq_len;
+        if (L <= pl.T1) {
+          info->single_pass_seqs++;
+          info->active_workgroups += num_kv_heads;
+        } else {
+          info->partitioned_seqs++;
+          info->active_workgroups += static_cast<long long>(num_kv_heads) *
+                                     ((L + pl.P - 1) / pl.P);
+        }
       }
     }
   }
@@ -256,10 +324,12 @@ PA_API int paged_attn_decode_ex(void* out, const void* q, const void* key_cache,
   args.vc = static_cast<const uint16_t*>(value_cache);
   args.bt = block_tables;
   args.seq_lens = seq_lens;
-  args.ws_acc = pl.ws_bytes ? static_cast<float*>(workspace) : nullptr;
-  args.ws_ml = pl.ws_bytes ? reinterpret_cast<float2*>(static_cast<char*>(workspace) +
-                                                       pl.ws_acc_bytes)
-                           : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  args.ws_acc = pl.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  args.ws_ml = pl.ws_bytes ? reinterpret_cast<float2*>(ws + pl.ws_ml_off) : nullptr;
+  args.jobs = pl.balanced && pl.ws_bytes ? reinterpret_cast<int2*>(ws + pl.ws_jobs_off) : nullptr;
+  args.records = pl.records;
+  args.num_wg = pl.num_wg;
   args.num_seqs = num_seqs;
   args.num_heads = num_heads;
   args.num_kv_heads = num_kv_heads;

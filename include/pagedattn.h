@@ -115,7 +115,8 @@ typedef struct pa_plan_info {
     int partitioned_seqs;      /* sequences split into partitions (needs host lengths) */
     size_t workspace_bytes;    /* bytes of workspace the call needs         */
     int threads_per_workgroup; /* phase-1 block size                        */
-    int lds_bytes_phase1;      /* static LDS of the phase-1 kernel          */
+    int lds_bytes_phase1;      /* LDS of the phase-1 tile slots             */
+    int balanced;              /* 1: length-balanced split (partition_size 0) */
 } pa_plan_info;
 
 /*

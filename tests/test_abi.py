@@ -90,8 +90,14 @@ def test_workspace_size_formula(lib):
     parts = 102400 // P
     acc = S * Hq * parts * D * 4
     assert n == ((acc + 255) // 256) * 256 + S * Hq * parts * 8
-    # enough (sequence, KV head) pairs for every compute unit: one pass each, no workspace
-    assert lib.paged_attn_workspace_size(256, 24, 4, 256, 32, 512, 16384, 0) == 0
+    # explicit partitions: every sequence fits one partition -> one pass, no workspace
+    assert lib.paged_attn_workspace_size(256, 24, 4, 256, 32, 512, 16384, 16384) == 0
+    # balanced split (partition_size 0): two records per phase-1 workgroup + a job each
+    nw = 512
+    recs = 2 * nw * 6
+    acc = ((recs * 256 * 4 + 255) // 256) * 256
+    ml = ((acc + recs * 8 + 255) // 256) * 256
+    assert lib.paged_attn_workspace_size(256, 24, 4, 256, 32, 512, 16384, 0) == ml + nw * 8
     assert lib.paged_attn_workspace_size(2, 24, 5, 256, 16, 64, 0, 512) == ctypes.c_size_t(-1).value
 
 
@@ -134,20 +140,46 @@ def test_tier_thresholds(lib):
     assert info["single_pass_seqs"] == 3 and info["phase2_workgroups"] == 0
 
 
-def test_automatic_partition_size_for_256_cus(lib):
-    """P = 0 spreads the step over one workgroup per compute unit."""
+def test_balanced_split_plan(lib):
+    """partition_size = 0: the step's tiles are cut into equal shares, two
+    workgroups per CU, whatever the length mix."""
     L = 102400
     info = pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0)          # 4 x 100K tokens
-    assert info["partition_size"] == 6400 and info["phase1_workgroups"] == 256
-    info = pa.plan([L], 24, 4, 256, 16, L // 16, L, 0)              # one 100K sequence
-    assert info["partition_size"] == 1600 and info["phase1_workgroups"] == 256
-    info = pa.plan([16384] * 256, 24, 4, 256, 32, 512, 16384, 0)    # 1024 (seq, kv) pairs
-    assert info["partition_size"] == 16384 and info["partitioned_seqs"] == 0
-    assert info["phase2_workgroups"] == 0 and info["workspace_bytes"] == 0
-    info = pa.plan([100] * 8, 24, 4, 256, 16, 8, 100, 0)            # short: one pass, P >= 256
-    assert info["partition_size"] == 112 and info["single_pass_seqs"] == 8
-    # a host-side total shrinks the partitions of an unequal batch
+    assert info["balanced"] == 1 and info["phase1_workgroups"] == 512
+    assert info["active_workgroups"] == 512 and info["partitioned_seqs"] == 4
+    assert info["phase2_workgroups"] == 512 * 4
+    # 1024 segments of 1024 tiles over 512 workgroups: shares end on segment ends
+    info = pa.plan([16384] * 256, 24, 4, 256, 32, 512, 16384, 0)
+    assert info["phase1_workgroups"] == 512
+    assert info["single_pass_seqs"] == 256 and info["partitioned_seqs"] == 0
+    # short: one workgroup per 16 tiles of the length bound
+    info = pa.plan([100] * 8, 24, 4, 256, 16, 8, 100, 0)
+    assert info["phase1_workgroups"] == (8 * 4 * 7 + 15) // 16
+    # a mix of very short and very long sequences: the long ones are cut into many
+    # shares; a short one is cut only where a share boundary happens to fall in it
     lens = [64] * 60 + [65536] * 4
+    info = pa.plan(lens, 24, 4, 256, 16, 4096, 65536, 0)
+    assert info["partitioned_seqs"] >= 4 and info["single_pass_seqs"] >= 50
+    assert info["partitioned_seqs"] + info["single_pass_seqs"] == 64
+    # zero-length sequences count as one pass
+    info = pa.plan([0, 0, 5000], 24, 4, 256, 16, 400, 5000, 0)
+    assert info["single_pass_seqs"] == 2 and info["partitioned_seqs"] == 1
+
+
+def test_automatic_partition_size_for_256_cus(lib):
+    """partition_size = 0 with a forced tier (or more sequences than the balanced
+    split handles) sizes fixed partitions for one workgroup per compute unit."""
+    L = 102400
+    info = pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0, single_pass_max_len=0)
+    assert info["balanced"] == 0
+    assert info["partition_size"] == 6400 and info["phase1_workgroups"] == 256
+    info = pa.plan([L], 24, 4, 256, 16, L // 16, L, 0, single_pass_max_len=0)
+    assert info["partition_size"] == 1600 and info["phase1_workgroups"] == 256
+    info = pa.plan([16384] * 2048, 24, 4, 256, 32, 512, 16384, 0)   # too many for the split
+    assert info["balanced"] == 0 and info["partition_size"] == 16384
+    assert info["partitioned_seqs"] == 0 and info["workspace_bytes"] == 0
+    # a host-side total shrinks the partitions of an unequal batch
+    lens = [64] * 1600 + [65536] * 4
     a = pa.plan(lens, 24, 4, 256, 16, 4096, 65536, 0)
     b = pa.plan(lens, 24, 4, 256, 16, 4096, 65536, 0, total_tokens_hint=sum(lens))
     per_cu = -(-sum(lens) * 4 // 256)

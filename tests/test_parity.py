@@ -53,24 +53,38 @@ def test_tiny(tier):
     assert_close(gpu_out(run(w, TIERS[tier])), oracle_full(w), f"tiny/{tier}")
 
 
-@pytest.mark.parametrize("tier", ["auto", "single"])
-def test_batch(tier):
-    say(f"case batch tier={tier}")
+# partition_size 512 (the pages' grid) and 0 (the length-balanced split)
+MODES = {"p512": 512, "balanced": 0}
+
+
+def test_tiny_balanced():
+    say("case tiny balanced")
+    w = workloads.tiny(device="cuda", poison=True)
+    assert pa.plan(list(w.seq_lens_host), 24, 4, 256, 16, w.max_blocks_per_seq,
+                   w.max_seq_len, 0)["balanced"] == 1
+    assert_close(gpu_out(run(w, P=0)), oracle_full(w), "tiny/balanced")
+
+
+@pytest.mark.parametrize("mode", ["auto", "single", "balanced"])
+def test_batch(mode):
+    say(f"case batch mode={mode}")
     w = workloads.batch(device="cuda", poison=True)
-    assert_close(gpu_out(run(w, TIERS[tier])), oracle_full(w), f"batch/{tier}")
+    out = run(w, P=0) if mode == "balanced" else run(w, TIERS[mode])
+    assert_close(gpu_out(out), oracle_full(w), f"batch/{mode}")
 
 
-def test_long_context_sampled():
-    say("case long 4x102400 P=512, oracle on sequences 0 and 3")
+@pytest.mark.parametrize("mode", list(MODES))
+def test_long_context_sampled(mode):
+    say(f"case long 4x102400 {mode}, oracle on sequences 0 and 3")
     w = workloads.long_context(device="cuda", poison=True)
-    out = gpu_out(run(w))
+    out = gpu_out(run(w, P=MODES[mode]))
     rows = [(s, h) for s in (0, 3) for h in range(w.num_heads)]
     ref = oracle_rows(w, rows)
     got = np.stack([out[s, h] for s, h in rows])
-    assert_close(got, ref, "long")
+    assert_close(got, ref, f"long/{mode}")
 
 
-@pytest.mark.parametrize("P", [256, 512, 1024])
+@pytest.mark.parametrize("P", [256, 512, 1024, 0])
 def test_mixed_sampled(P):
     say(f"case mixed 64 seqs bf16 P={P}")
     w = workloads.mixed(device="cuda", poison=True, partition_size=P)
@@ -83,16 +97,39 @@ def test_mixed_sampled(P):
     assert_close(got, ref, f"mixed/P={P} lens={[int(w.seq_lens_host[s]) for s in seqs]}")
 
 
-def test_saturation_sampled():
-    say("case saturation 256x16384 bs=32, 150000-page pool, oracle on 3 sequences")
+@pytest.mark.parametrize("mode", list(MODES))
+def test_saturation_sampled(mode):
+    say(f"case saturation 256x16384 bs=32 {mode}, 150000-page pool, oracle on 3 sequences")
     w = workloads.saturation(device="cuda", poison=False)
-    out = gpu_out(run(w))
+    out = gpu_out(run(w, P=MODES[mode]))
     rows = [(s, h) for s in (0, 137, 255) for h in range(w.num_heads)]
     ref = oracle_rows(w, rows)
     got = np.stack([out[s, h] for s, h in rows])
-    assert_close(got, ref, "saturation")
+    assert_close(got, ref, f"saturation/{mode}")
     del w
     torch.cuda.empty_cache()
+
+
+def test_balanced_many_short_sequences():
+    """Hundreds of short segments per share, zero-length sequences in between."""
+    say("case balanced: 300 short sequences with zeros")
+    rng = np.random.default_rng(31)
+    lens = rng.integers(0, 120, size=300)
+    lens[::17] = 0
+    w = make(list(lens), partition_size=0, seed=31)
+    out = gpu_out(run(w, P=0))
+    assert np.all(out[lens == 0] == 0)
+    assert_close(out, oracle_full(w), "balanced/short")
+
+
+def test_balanced_falls_back_above_sequence_cap():
+    """More sequences than the balanced split keeps in LDS: fixed partitions."""
+    say("case 1600 sequences, partition_size 0")
+    lens = [5 + (i * 37) % 200 for i in range(1600)]
+    w = make(lens, num_heads=8, num_kv_heads=4, head_dim=128, scale=1 / math.sqrt(128),
+             partition_size=0, seed=32)
+    assert pa.plan(lens, 8, 4, 128, 16, w.max_blocks_per_seq, w.max_seq_len, 0)["balanced"] == 0
+    assert_close(gpu_out(run(w, P=0)), oracle_full(w), "fallback")
 
 
 # ---------------------------------------------------------------------------
@@ -112,21 +149,22 @@ def test_partition_sizes(dtype, bs, P):
 
 @pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("heads", [(8, 8), (16, 8), (16, 4), (32, 4), (64, 4), (16, 1)])
-@pytest.mark.parametrize("tier", ["single", "partitioned"])
+@pytest.mark.parametrize("tier", ["single", "partitioned", "balanced"])
 def test_head_shapes(D, heads, tier):
     Hq, Hkv = heads
     say(f"case heads Hq={Hq} Hkv={Hkv} D={D} tier={tier}")
     w = make([5, 260, 777], num_heads=Hq, num_kv_heads=Hkv, head_dim=D,
              scale=1 / math.sqrt(D), partition_size=256)
-    assert_close(gpu_out(run(w, TIERS[tier])), oracle_full(w), f"Hq{Hq}/Hkv{Hkv}/D{D}")
+    out = run(w, P=0) if tier == "balanced" else run(w, TIERS[tier])
+    assert_close(gpu_out(out), oracle_full(w), f"Hq{Hq}/Hkv{Hkv}/D{D}/{tier}")
 
 
-@pytest.mark.parametrize("tier", ["single", "partitioned"])
+@pytest.mark.parametrize("tier", ["single", "partitioned", "balanced"])
 def test_edge_lengths(tier):
     lens = [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1023, 1024, 1025, 0, 2]
     say(f"case edge lengths tier={tier}")
     w = make(lens, partition_size=512)
-    out = gpu_out(run(w, TIERS[tier]))
+    out = gpu_out(run(w, P=0) if tier == "balanced" else run(w, TIERS[tier]))
     assert np.all(out[0] == 0) and np.all(out[17] == 0)
     assert_close(out, oracle_full(w), f"edges/{tier}")
 
@@ -151,8 +189,8 @@ def test_outlier_rows_rescale():
 def test_seq_len_one_is_v_bitwise(dtype):
     say(f"case L=1 dtype={dtype}")
     w = make([1, 1, 1], dtype=dtype)
-    for tier in ("single", "partitioned"):
-        out = run(w, TIERS[tier])
+    for tier in ("single", "partitioned", "balanced"):
+        out = run(w, P=0) if tier == "balanced" else run(w, TIERS[tier])
         torch.cuda.synchronize()
         g = w.num_heads // w.num_kv_heads
         for s in range(3):
@@ -188,6 +226,10 @@ def test_deterministic_and_relabel_invariant():
     b = run(w).clone()
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+    c0 = run(w, P=0).clone()
+    c1 = run(w, P=0).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(c0, c1)
     perm = torch.randperm(w.num_blocks, generator=torch.Generator().manual_seed(3))
     inv = torch.argsort(perm)
     kc = w.key_cache[perm.cuda()]
@@ -228,8 +270,8 @@ def test_needle_high_page_ids():
         for s in range(2):
             page = int(bt[s, t // bs])
             kc[page, :, t % bs, 0] = 32.0
-        for tier in (ALL_SINGLE, 0):
-            out = pa.decode(q, kc, vc, bt, sl, 1.0 / 16, partition_size=512, max_seq_len=L,
+        for tier, P in ((ALL_SINGLE, 512), (0, 512), (None, 0)):
+            out = pa.decode(q, kc, vc, bt, sl, 1.0 / 16, partition_size=P, max_seq_len=L,
                             single_pass_max_len=tier)
             torch.cuda.synchronize()
             for s in range(2):
