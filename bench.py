@@ -109,6 +109,10 @@ def main():
     ap.add_argument("--p512", action="store_true",
                     help="also time the pages' fixed 512-token partitions (context only)")
     ap.add_argument("--single-pass-max-len", type=int, default=None)
+    ap.add_argument("--no-hint", action="store_true",
+                    help="do not pass the host-side total of seq_lens to the planner")
+    ap.add_argument("--num-cus", type=int, default=0,
+                    help="compute units assumed by the automatic choices (0 = 256)")
     ap.add_argument("--cpu-seqs", type=int, default=4,
                     help="sequences of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu", action="store_true")
@@ -139,13 +143,17 @@ def main():
     def decoder(P):
         return pa.Decoder(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size,
                           w.max_blocks_per_seq, w.q.dtype, max_seq_len=w.max_seq_len,
-                          partition_size=P, single_pass_max_len=args.single_pass_max_len)
+                          partition_size=P, single_pass_max_len=args.single_pass_max_len,
+                          num_cus=args.num_cus, total_tokens_hint=total)
 
     P = args.partition_size
+    # the caller knows its sequence lengths on the host: pass their sum
+    total = 0 if args.no_hint else int(w.seq_lens_host.clip(0).astype("int64").sum())
     dec = decoder(P)
     info = pa.plan(list(w.seq_lens_host), w.num_heads, w.num_kv_heads, w.head_dim,
                    w.block_size, w.max_blocks_per_seq, w.max_seq_len, P,
-                   single_pass_max_len=args.single_pass_max_len)
+                   single_pass_max_len=args.single_pass_max_len, num_cus=args.num_cus,
+                   total_tokens_hint=total)
     log(f"plan: {info}")
 
     if args.copy_probe_mib > 0:
@@ -241,6 +249,7 @@ def main():
                    "partition_size": info["partition_size"],
                    "partition_size_arg": P,
                    "single_pass_max_len": info["single_pass_max_len"],
+                   "split": "balanced" if info["balanced"] else "fixed partitions",
                    "kv_bytes_per_step": kv, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "pa_phase1_kernel",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -122,8 +122,8 @@ def plan(seq_lens_host, num_heads: int, num_kv_heads: int, head_dim: int, block_
 def workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
                    block_size: int, max_blocks_per_seq: int, max_seq_len: int = 0,
                    partition_size: int = 0, single_pass_max_len: Optional[int] = None,
-                   total_tokens_hint: int = 0) -> int:
-    o = _opts(single_pass_max_len, total_tokens_hint=total_tokens_hint)
+                   total_tokens_hint: int = 0, num_cus: int = 0) -> int:
+    o = _opts(single_pass_max_len, num_cus, total_tokens_hint=total_tokens_hint)
     n = lib().paged_attn_workspace_size_ex(num_seqs, num_heads, num_kv_heads, head_dim,
                                            block_size, max_blocks_per_seq, max_seq_len,
                                            partition_size, ctypes.byref(o))
@@ -143,16 +143,16 @@ class Decoder:
                  block_size: int, max_blocks_per_seq: int, dtype: torch.dtype,
                  max_seq_len: int = 0, partition_size: int = 0,
                  single_pass_max_len: Optional[int] = None, total_tokens_hint: int = 0,
-                 device="cuda"):
+                 num_cus: int = 0, device="cuda"):
         self.shape = (num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                       max_blocks_per_seq)
         self.dtype = dtype
         self.max_seq_len = int(max_seq_len)
         self.partition_size = int(partition_size)
-        self.opts = _opts(single_pass_max_len, total_tokens_hint=total_tokens_hint)
+        self.opts = _opts(single_pass_max_len, num_cus, total_tokens_hint=total_tokens_hint)
         nbytes = workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                                 max_blocks_per_seq, max_seq_len, partition_size,
-                                single_pass_max_len, total_tokens_hint)
+                                single_pass_max_len, total_tokens_hint, num_cus)
         self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
         self.workspace_bytes = nbytes
         self.out = torch.empty((num_seqs, num_heads, head_dim), dtype=dtype, device=device)

@@ -23,11 +23,11 @@
 //  - pa_phase1_kernel: the pages' grid (sequence, KV head, partition) with a
 //    fixed partition size; a sequence no longer than the single-pass bound is
 //    one piece (page of commit b80fd2b, three-tier decode dispatch).
-//  - pa_phase1_balanced_kernel: the step's tiles, (sequence, KV head) segments
-//    laid end to end, are cut into one equal share per workgroup, computed on
-//    the device from seq_lens.  A segment inside one share is one pass; a
-//    segment crossing shares is partitioned at the share boundaries.  Every
-//    workgroup then streams the same number of bytes whatever the length mix.
+//  - pa_phase1_balanced_kernel: the step's tiles, sequences laid end to end, are
+//    cut into equal shares computed on the device from seq_lens, one workgroup
+//    per (share, KV head).  A sequence inside one share is one pass; a sequence
+//    crossing shares is partitioned at the share boundaries.  Every workgroup
+//    then streams the same number of bytes whatever the length mix.
 //
 // Phase 2 (pa_reduce_kernel) merges the partials of each partitioned segment
 // with the rescale of the online-softmax fix (page of commit 87a19d2): with M
@@ -99,8 +99,8 @@ struct BF16 {
 // one 16-wide slice back to back) and ws_ml is [R][G] float2.
 //  - grid mode:     record (s*Hkv + kvh)*max_parts + partition, R = S*Hkv*max_parts
 //  - balanced mode: record 2*w + slot of workgroup w (slot 0: the piece that
-//                   ends a segment begun earlier, slot 1: the piece that begins a
-//                   segment continued later), R = 2*num_wg
+//                   ends a sequence begun in an earlier share, slot 1: the piece
+//                   that begins a sequence continued in a later share), R = 2*num_wg
 struct DecodeArgs {
   void* out;
   const uint16_t* q;
@@ -140,7 +140,10 @@ struct GatherArgs {
   int max_seq_len;
 };
 
-constexpr int kMaxBalancedSeqs = 1536;   // balanced mode keeps a prefix of seq_lens in LDS
+#ifndef PA_MAX_BALANCED_SEQS
+#define PA_MAX_BALANCED_SEQS 1024
+#endif
+constexpr int kMaxBalancedSeqs = PA_MAX_BALANCED_SEQS;   // balanced mode keeps a prefix of seq_lens in LDS
 
 __device__ __forceinline__ size_t rec_acc_index(int slice, long long rec, int h, int G,
                                                 long long R) {
@@ -151,12 +154,23 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int s) {
   return min(a.seq_lens[s], a.max_seq_len);
 }
 
-// Element offset of token t0 (a multiple of 16) of KV head kvh of sequence s.
-// 64-bit: pools above 4 G elements are legal.  The page id is wave-uniform.
+// Element offset of the 16-token tile starting at token t0 (a multiple of 16) of KV
+// head kvh, given the page that holds it.  64-bit: pools above 4 G elements are legal.
+__device__ __forceinline__ size_t tile_offset_in(int page, int t0, int kvh, int Hkv, int bs,
+                                                 int D) {
+  const unsigned slot = static_cast<unsigned>(t0) % static_cast<unsigned>(bs);
+  return ((static_cast<size_t>(page) * Hkv + kvh) * bs + slot) * static_cast<size_t>(D);
+}
+
+// Page holding token t0 of sequence s (wave-uniform).
+__device__ __forceinline__ int page_of(const int32_t* bt, int s, int t0, int bs, int mbps) {
+  const unsigned blk = static_cast<unsigned>(t0) / static_cast<unsigned>(bs);
+  return __builtin_amdgcn_readfirstlane(bt[(size_t)s * mbps + blk]);
+}
+
 __device__ __forceinline__ size_t tile_offset(const int32_t* bt, int s, int t0, int kvh,
                                               int Hkv, int bs, int mbps, int D) {
-  const int page = __builtin_amdgcn_readfirstlane(bt[(size_t)s * mbps + t0 / bs]);
-  return ((static_cast<size_t>(page) * Hkv + kvh) * bs + (t0 % bs)) * static_cast<size_t>(D);
+  return tile_offset_in(page_of(bt, s, t0, bs, mbps), t0, kvh, Hkv, bs, D);
 }
 
 // One 16-token tile is 16*D*2 bytes, contiguous.  Lane `lane` fetches the 16-byte
@@ -229,28 +243,43 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& 
   const int col = lane & 15;     // query head (QK^T/PV columns) or row index within a tile
   const int grp = lane >> 4;     // 4-lane-group index: k-slot block / 4-row block
 
-  // the wave's first tile is requested before Q is staged, so the two latencies overlap
+  // Loads are issued in the order they are needed, because vector-memory counters
+  // retire in order: the group's Q rows, the page ids of the wave's first two tiles,
+  // then the first tile.  Page ids then run one tile ahead of the K/V loads, so a
+  // block-table round trip never sits between two tiles.
+  constexpr int QLOADS = (kTile * D / 8 + W * 64 - 1) / (W * 64);
+  u32x4 qv[QLOADS];
+  {
+    const uint16_t* qg = a.q + ((size_t)s * Hq + (size_t)kvh * G) * D;
+#pragma unroll
+    for (int j = 0; j < QLOADS; ++j) {
+      const int i = threadIdx.x + j * W * 64;
+      const int row = i / Z::kChunks, c = i % Z::kChunks;
+      qv[j] = u32x4{0, 0, 0, 0};
+      if (i < kTile * Z::kChunks && row < G)
+        qv[j] = *reinterpret_cast<const u32x4*>(qg + row * D + 8 * c);
+    }
+  }
   const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
-  u32x4 rk[LOADS], rv[LOADS];
+  const int bs = a.block_size, mbps = a.max_blocks_per_seq;
   int it = wave;
+  int page_cur = it < n_tiles ? page_of(a.bt, s, t_begin + kTile * it, bs, mbps) : 0;
+  int page_next = it + W < n_tiles ? page_of(a.bt, s, t_begin + kTile * (it + W), bs, mbps) : 0;
+  u32x4 rk[LOADS], rv[LOADS];
   if (it < n_tiles) {
-    const size_t off = tile_offset(a.bt, s, t_begin + kTile * it, kvh, Hkv, a.block_size,
-                                   a.max_blocks_per_seq, D);
+    const size_t off = tile_offset_in(page_cur, t_begin + kTile * it, kvh, Hkv, bs, D);
     load_tile<D>(a.kc + off, lane, rk);
     load_tile<D>(a.vc + off, lane, rv);
   }
 
-  // Q of the group, staged once in LDS as the B operand of S^T = K Q^T: row h is
-  // query head kvh*G + h (rows G..15 are zero), swizzled like a K tile.
-  __syncthreads();
-  {
-    const uint16_t* qg = a.q + ((size_t)s * Hq + (size_t)kvh * G) * D;
-    for (int i = threadIdx.x; i < kTile * Z::kChunks; i += W * 64) {
-      const int row = i / Z::kChunks, c = i % Z::kChunks;
-      u32x4 v = {0, 0, 0, 0};
-      if (row < G) v = *reinterpret_cast<const u32x4*>(qg + row * D + 8 * c);
-      *reinterpret_cast<u32x4*>(sm.q + Z::byte_off(row, c)) = v;
-    }
+  // Q of the group in LDS as the B operand of S^T = K Q^T: row h is query head
+  // kvh*G + h (rows G..15 are zero), swizzled like a K tile.
+  __syncthreads();                 // LDS of a previous piece may still be read
+#pragma unroll
+  for (int j = 0; j < QLOADS; ++j) {
+    const int i = threadIdx.x + j * W * 64;
+    if (i < kTile * Z::kChunks)
+      *reinterpret_cast<u32x4*>(sm.q + Z::byte_off(i / Z::kChunks, i % Z::kChunks)) = qv[j];
   }
   __syncthreads();
 
@@ -276,12 +305,13 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& 
       *reinterpret_cast<u32x4*>(ldsV + off) = rv[j];
     }
     wave_lds_fence();
-    // prefetch the wave's next tile while this one is consumed
+    // prefetch the wave's next tile while this one is consumed, and the page id of
+    // the one after
     if (it + W < n_tiles) {
-      const size_t off = tile_offset(a.bt, s, t0 + kTile * W, kvh, Hkv, a.block_size,
-                                     a.max_blocks_per_seq, D);
+      const size_t off = tile_offset_in(page_next, t0 + kTile * W, kvh, Hkv, bs, D);
       load_tile<D>(a.kc + off, lane, rk);
       load_tile<D>(a.vc + off, lane, rv);
+      if (it + 2 * W < n_tiles) page_next = page_of(a.bt, s, t0 + 2 * kTile * W, bs, mbps);
     }
 
     // S^T[token, head] = sum_d K[token, d] Q[head, d]
@@ -423,23 +453,28 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_kernel(DecodeArgs a) 
   run_piece<D, DT, W>(a, sm, s, kvh, t_begin, t_end, single, rec);
 }
 
-// Balanced mode.  Segment q = s*Hkv + kvh has n(s) = ceil(L_s/16) tiles; segments
-// are laid end to end (q order) into T tiles, and workgroup w takes tiles
-// [T*w/NW, T*(w+1)/NW).  Each workgroup rebuilds the per-sequence prefix of
-// tiles in LDS from seq_lens (S <= kMaxBalancedSeqs), then walks its share.
+// Balanced mode.  Sequence s has n(s) = ceil(L_s/16) tiles per KV head; laid end
+// to end they make T tiles, cut into NS = num_wg/Hkv equal shares.  Workgroup w
+// takes share j = w / Hkv of KV head kvh = w % Hkv, so the Hkv workgroups of a
+// share run side by side and read the Hkv contiguous chunks of the same pages.
+// Each workgroup rebuilds the per-sequence prefix of tiles in LDS from seq_lens
+// (S <= kMaxBalancedSeqs), then walks its share.
 template <int D, class DT, int W>
 __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(DecodeArgs a) {
   constexpr int NT = W * 64;
   constexpr int PER = kMaxBalancedSeqs / NT;
   __shared__ __attribute__((aligned(16))) Phase1Lds<D, W> sm;
   __shared__ int pre[kMaxBalancedSeqs + 1];     // pre[s] = tiles of sequences < s (one KV head)
+  __shared__ unsigned char last_len[kMaxBalancedSeqs];   // tokens in a sequence's last tile
   __shared__ int wave_tot[W];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int S = a.num_seqs, Hkv = a.num_kv_heads;
-  const int w = blockIdx.x, NW = a.num_wg;
+  const int w = blockIdx.x;
+  const int NS = a.num_wg / Hkv;
+  const int j = w / Hkv, kvh = w % Hkv;
 
   // ---- inclusive scan of tiles per sequence: thread tid owns sequences tid*PER ..
   int local[PER];
@@ -451,6 +486,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(Decod
     if (s < S) {
       const int L = clamp_len(a, s);
       n = L > 0 ? (L + kTile - 1) / kTile : 0;
+      last_len[s] = static_cast<unsigned char>(L > 0 ? L - kTile * (n - 1) : 0);
     }
     tsum += n;
     local[i] = tsum;
@@ -473,11 +509,11 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(Decod
   if (tid == 0) pre[0] = 0;
   __syncthreads();
 
-  const long long T = (long long)Hkv * pre[S];
-  const long long lo = T * w / NW, hi = T * (w + 1) / NW;
+  const long long T = pre[S];
+  const long long lo = T * j / NS, hi = T * (j + 1) / NS;
 
   // sequences of length <= 0 get zero rows; spread over the workgroups
-  for (int s = w; s < S; s += NW) {
+  for (int s = w; s < S; s += a.num_wg) {
     if (pre[s + 1] == pre[s]) {
       uint16_t* o = static_cast<uint16_t*>(a.out) + (size_t)s * a.num_heads * D;
       for (int i = tid; i < a.num_heads * D / 8; i += NT)
@@ -487,38 +523,35 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(Decod
 
   int2 job = make_int2(-1, 0);
   if (lo == hi) {
-    // an empty share (fewer tiles than workgroups) may lie inside a segment that
-    // neighbouring workgroups split: leave the identity (-inf, 0) in slot 0
+    // an empty share (fewer tiles than shares) may lie inside a sequence that
+    // neighbouring shares split: leave the identity (-inf, 0) in slot 0
     for (int h = tid; h < a.group; h += NT)
       a.ws_ml[2LL * w * a.group + h] = make_float2(kNegInf, 0.f);
   } else {
-    // the sequence holding tile lo: largest s with Hkv*pre[s] <= lo (it has tiles)
+    // the sequence holding tile lo: largest s with pre[s] <= lo (it has tiles)
     int s = 0, top = S - 1;
     while (s < top) {
       const int mid = (s + top + 1) >> 1;
-      if ((long long)Hkv * pre[mid] <= lo) s = mid; else top = mid - 1;
+      if (pre[mid] <= lo) s = mid; else top = mid - 1;
     }
     long long x = lo;
     while (x < hi) {
-      const int n = pre[s + 1] - pre[s];
-      const long long seq0 = (long long)Hkv * pre[s];
-      const int kvh = (int)((x - seq0) / n);
-      const long long seg0 = seq0 + (long long)kvh * n, seg1 = seg0 + n;
-      const int ta = (int)(x - seg0);
-      const int tb = (int)(min(hi, seg1) - seg0);
+      const long long seg0 = pre[s], seg1 = pre[s + 1];
+      const int n = static_cast<int>(seg1 - seg0);
+      const int ta = static_cast<int>(x - seg0);
+      const int tb = static_cast<int>(min(hi, seg1) - seg0);
       const bool final = ta == 0 && tb == n;
       const long long rec = 2LL * w + (ta > 0 ? 0 : 1);
       if (ta == 0 && !final) {
-        // this workgroup starts a segment that later ones continue: it owns the merge
-        const long long last = (seg1 * NW - 1) / T;      // workgroup holding tile seg1-1
-        job = make_int2(s * Hkv + kvh, (int)(last - w + 1));
+        // this share starts a sequence that later shares continue: it owns the merge
+        const long long last = (seg1 * NS - 1) / T;      // share holding tile seg1-1
+        job = make_int2(s * Hkv + kvh, static_cast<int>(last - j + 1));
       }
-      const int L = clamp_len(a, s);
-      run_piece<D, DT, W>(a, sm, s, kvh, kTile * ta, min(L, kTile * tb), final, rec);
+      // the piece ends at its last tile, or at the sequence's last token
+      const int t_end = tb == n ? kTile * (n - 1) + last_len[s] : kTile * tb;
+      run_piece<D, DT, W>(a, sm, s, kvh, kTile * ta, t_end, final, rec);
       x = seg1 < hi ? seg1 : hi;
-      if (kvh + 1 == Hkv) {
-        do { ++s; } while (s < S && pre[s + 1] == pre[s] && x < hi);
-      }
+      do { ++s; } while (s < S && pre[s + 1] == pre[s] && x < hi);
     }
   }
   if (tid == 0) a.jobs[w] = job;
@@ -554,7 +587,8 @@ __device__ __forceinline__ void combine_into(Partial& x, float om, float ow, f32
 //   grid mode (BAL = false): workgroup (segment q, slice group), partials
 //     q*max_parts + p for p < ceil(L/P); segments in one pass are skipped.
 //   balanced mode (BAL = true): workgroup (w, slice group) merges the segment
-//     begun by phase-1 workgroup w, if any: record 2w+1, then 2(w+p) for p >= 1.
+//     begun by phase-1 workgroup w, if any: record 2w+1, then 2(w+p*Hkv) for
+//     p >= 1 (the same KV head in the following shares).
 template <int D, class DT, int G, int SPW, bool BAL>
 __global__ __launch_bounds__(kRedThreads) void pa_reduce_kernel(DecodeArgs a) {
   constexpr int NSG = D / 16 / SPW;        // slice groups per segment
@@ -580,7 +614,7 @@ __global__ __launch_bounds__(kRedThreads) void pa_reduce_kernel(DecodeArgs a) {
     q = job.x;
     np = job.y;
     rec0 = 2LL * unit;
-    step = 2;
+    step = 2LL * Hkv;
     first = 1;
   } else {
     q = unit;

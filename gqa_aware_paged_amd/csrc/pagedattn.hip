@@ -31,7 +31,7 @@ constexpr int kDefaultCUs = 256;            // MI355X
 constexpr float kLog2e = 1.4426950408889634f;
 
 constexpr int kMinTilesPerWG = 16;        // balanced mode: at least 4 tiles per wave
-constexpr int kBalancedSlices = 4;        // balanced phase 2: 16-wide slices per workgroup
+constexpr int kBalancedSlices = 8;        // balanced phase 2: 16-wide slices per workgroup
 
 struct Plan {
   bool balanced = false; // length-balanced split (partition_size 0) vs fixed partitions
@@ -88,20 +88,26 @@ int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int 
   pl.max_seq_len = max_len > 0 ? max_len : mbps * bs;
   const int cus = (opt && opt->num_cus > 0) ? opt->num_cus : kDefaultCUs;
   const bool forced_tier = opt && opt->single_pass_max_len >= 0;
-  pl.balanced = P_req == 0 && !forced_tier && S <= pa::kMaxBalancedSeqs;
+  // a host-side total equal to num_seqs * max_seq_len means every sequence is at
+  // the bound: fixed partitions of one workgroup per CU are then exactly balanced
+  // and need no device-side prefix of seq_lens
+  const long long hint = opt ? opt->total_tokens_hint : 0;
+  const bool uniform = hint > 0 && hint == static_cast<long long>(S) * pl.max_seq_len;
+  pl.balanced = P_req == 0 && !forced_tier && !uniform && S <= pa::kMaxBalancedSeqs;
   if (pl.balanced) {
-    // two resident workgroups per CU, but at least kMinTilesPerWG tiles each
-    const long long tiles = static_cast<long long>(S) * Hkv * ((pl.max_seq_len + 15) / 16);
-    long long nw = (tiles + kMinTilesPerWG - 1) / kMinTilesPerWG;
-    if (nw > 2LL * cus) nw = 2LL * cus;
-    if (nw < 1) nw = 1;
-    pl.num_wg = static_cast<int>(nw);
+    // shares x KV heads: about two resident workgroups per CU, but at least
+    // kMinTilesPerWG tiles per workgroup
+    const long long tiles = static_cast<long long>(S) * ((pl.max_seq_len + 15) / 16);
+    long long ns = (tiles + kMinTilesPerWG - 1) / kMinTilesPerWG;
+    const long long ns_max = (2LL * cus) / Hkv > 0 ? (2LL * cus) / Hkv : 1;
+    if (ns > ns_max) ns = ns_max;
+    if (ns < 1) ns = 1;
+    pl.num_wg = static_cast<int>(ns * Hkv);
     pl.records = 2LL * pl.num_wg;
     pl.grid1 = pl.num_wg;
     pl.grid2 = static_cast<long long>(pl.num_wg) * (D / 16 / kBalancedSlices);
     pl.T1 = -1;
   } else {
-    const long long hint = opt ? opt->total_tokens_hint : 0;
     pl.P = P_req > 0 ? P_req : auto_partition(S, Hkv, pl.max_seq_len, cus, hint);
     // a sequence that fits in one partition is served in one pass
     pl.T1 = forced_tier ? opt->single_pass_max_len : pl.P;
@@ -252,29 +258,26 @@ PA_API int paged_attn_plan(const int32_t* seq_lens_host, int num_seqs, int num_h
   info->balanced = pl.balanced ? 1 : 0;
   if (seq_lens_host) {
     if (pl.balanced) {
-      // host mirror of the device split: segment q = s*Hkv + kvh covers tiles
-      // [start, start + n) of T; workgroup w takes [T*w/NW, T*(w+1)/NW)
+      // host mirror of the device split: sequence s covers tiles [pre_s, pre_s + n)
+      // of T; share j takes [T*j/NS, T*(j+1)/NS), one workgroup per KV head
       long long T = 0;
       for (int s = 0; s < num_seqs; ++s) {
         const int L = seq_lens_host[s] < pl.max_seq_len ? seq_lens_host[s] : pl.max_seq_len;
-        T += static_cast<long long>(num_kv_heads) * (L > 0 ? (L + 15) / 16 : 0);
+        T += L > 0 ? (L + 15) / 16 : 0;
       }
-      const long long NW = pl.num_wg;
+      const long long NS = pl.num_wg / num_kv_heads;
       long long start = 0;
       for (int s = 0; s < num_seqs; ++s) {
         const int L = seq_lens_host[s] < pl.max_seq_len ? seq_lens_host[s] : pl.max_seq_len;
         const long long n = L > 0 ? (L + 15) / 16 : 0;
-        bool split = false;
-        for (int kvh = 0; kvh < num_kv_heads && n > 0; ++kvh, start += n) {
-          const long long first = ((start + 1) * NW - 1) / T;
-          const long long last = ((start + n) * NW - 1) / T;
-          split = split || first != last;
-        }
-        if (split) info->partitioned_seqs++;
-        else info->single_pass_seqs++;
+        if (n > 0 && ((start + 1) * NS - 1) / T != ((start + n) * NS - 1) / T)
+          info->partitioned_seqs++;
+        else
+          info->single_pass_seqs++;
+        start += n;
       }
-      for (long long w = 0; w < NW; ++w)
-        if (T * w / NW < T * (w + 1) / NW) info->active_workgroups++;
+      for (long long j = 0; j < NS; ++j)
+        if (T * j / NS < T * (j + 1) / NS) info->active_workgroups += num_kv_heads;
     } else {
       for (int s = 0; s < num_seqs; ++s) {
         const int L = seq_lens_host[s] < pl.max_seq_len ? seq_lens_host[s] : pl.max_seq_len;

@@ -93,7 +93,10 @@ typedef struct pa_options {
     /* Compute units assumed by the automatic choices; <= 0 means 256 (MI355X). */
     int num_cus;
     /* Sum of seq_lens if the caller knows it on the host (0 = unknown).  Only
-     * used to size automatic partitions for batches of unequal lengths. */
+     * used when partition_size is 0: a total of num_seqs * max_seq_len (every
+     * sequence at the bound) selects fixed partitions of one workgroup per CU
+     * instead of the device-side balanced split; with a forced tier it sizes the
+     * automatic partitions. */
     long long total_tokens_hint;
     int reserved[4];
     /* If non-NULL, hipEventRecord(phase1_begin/phase1_end, stream) is issued
@@ -153,9 +156,15 @@ size_t paged_attn_workspace_size_ex(int num_seqs, int num_heads, int num_kv_head
  *   head_dim, block_size      see "Supported shapes"
  *   scale               multiplies q.k in fp32 (typically 1/sqrt(head_dim))
  *   partition_size      tokens per phase-1 partition of a long sequence (a positive
- *                       multiple of 16), or 0: ceil(num_seqs * max_seq_len *
- *                       num_kv_heads / 256) rounded up to 16, at least 256 and at
- *                       most max_seq_len (one workgroup per compute unit)
+ *                       multiple of 16: the pages' fixed-partition grid), or 0:
+ *                       automatic.  Automatic is the length-balanced split (the
+ *                       step's tiles cut on the device into equal shares, one
+ *                       workgroup per share and KV head, about two per CU) for up
+ *                       to 1024 sequences; with equal lengths declared through
+ *                       pa_options.total_tokens_hint, more sequences, or a forced
+ *                       tier, it is fixed partitions of ceil(num_seqs *
+ *                       max_seq_len * num_kv_heads / 256) tokens rounded up to 16,
+ *                       at least 256 and at most max_seq_len
  *   workspace           device scratch of workspace_bytes bytes (may be NULL when
  *                       paged_attn_workspace_size(...) == 0); not read before written
  *   stream              hipStream_t to enqueue on

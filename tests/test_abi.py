@@ -147,14 +147,14 @@ def test_balanced_split_plan(lib):
     info = pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0)          # 4 x 100K tokens
     assert info["balanced"] == 1 and info["phase1_workgroups"] == 512
     assert info["active_workgroups"] == 512 and info["partitioned_seqs"] == 4
-    assert info["phase2_workgroups"] == 512 * 4
+    assert info["phase2_workgroups"] == 512 * 2
     # 1024 segments of 1024 tiles over 512 workgroups: shares end on segment ends
     info = pa.plan([16384] * 256, 24, 4, 256, 32, 512, 16384, 0)
     assert info["phase1_workgroups"] == 512
     assert info["single_pass_seqs"] == 256 and info["partitioned_seqs"] == 0
     # short: one workgroup per 16 tiles of the length bound
     info = pa.plan([100] * 8, 24, 4, 256, 16, 8, 100, 0)
-    assert info["phase1_workgroups"] == (8 * 4 * 7 + 15) // 16
+    assert info["phase1_workgroups"] == 4 * ((8 * 7 + 15) // 16)   # shares x KV heads
     # a mix of very short and very long sequences: the long ones are cut into many
     # shares; a short one is cut only where a share boundary happens to fall in it
     lens = [64] * 60 + [65536] * 4
@@ -167,19 +167,25 @@ def test_balanced_split_plan(lib):
 
 
 def test_automatic_partition_size_for_256_cus(lib):
-    """partition_size = 0 with a forced tier (or more sequences than the balanced
-    split handles) sizes fixed partitions for one workgroup per compute unit."""
+    """partition_size = 0 with equal lengths declared, a forced tier, or more
+    sequences than the balanced split handles: fixed partitions for one workgroup
+    per compute unit."""
     L = 102400
+    info = pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0, total_tokens_hint=4 * L)
+    assert info["balanced"] == 0 and info["partition_size"] == 6400
+    info = pa.plan([L] * 3 + [L - 1], 24, 4, 256, 16, L // 16, L, 0,
+                   total_tokens_hint=4 * L - 1)
+    assert info["balanced"] == 1
     info = pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0, single_pass_max_len=0)
     assert info["balanced"] == 0
     assert info["partition_size"] == 6400 and info["phase1_workgroups"] == 256
     info = pa.plan([L], 24, 4, 256, 16, L // 16, L, 0, single_pass_max_len=0)
     assert info["partition_size"] == 1600 and info["phase1_workgroups"] == 256
-    info = pa.plan([16384] * 2048, 24, 4, 256, 32, 512, 16384, 0)   # too many for the split
+    info = pa.plan([16384] * 1100, 24, 4, 256, 32, 512, 16384, 0)   # too many for the split
     assert info["balanced"] == 0 and info["partition_size"] == 16384
     assert info["partitioned_seqs"] == 0 and info["workspace_bytes"] == 0
     # a host-side total shrinks the partitions of an unequal batch
-    lens = [64] * 1600 + [65536] * 4
+    lens = [64] * 1100 + [65536] * 4
     a = pa.plan(lens, 24, 4, 256, 16, 4096, 65536, 0)
     b = pa.plan(lens, 24, 4, 256, 16, 4096, 65536, 0, total_tokens_hint=sum(lens))
     per_cu = -(-sum(lens) * 4 // 256)

@@ -124,8 +124,8 @@ def test_balanced_many_short_sequences():
 
 def test_balanced_falls_back_above_sequence_cap():
     """More sequences than the balanced split keeps in LDS: fixed partitions."""
-    say("case 1600 sequences, partition_size 0")
-    lens = [5 + (i * 37) % 200 for i in range(1600)]
+    say("case 1100 sequences, partition_size 0")
+    lens = [5 + (i * 37) % 200 for i in range(1100)]
     w = make(lens, num_heads=8, num_kv_heads=4, head_dim=128, scale=1 / math.sqrt(128),
              partition_size=0, seed=32)
     assert pa.plan(lens, 8, 4, 128, 16, w.max_blocks_per_seq, w.max_seq_len, 0)["balanced"] == 0
