@@ -185,14 +185,23 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ src, int 
   for (int j = 0; j < D / 32; ++j) r[j] = __builtin_nontemporal_load(s4 + j * 64 + lane);
 }
 
-// LDS slot of one tile: 16 rows of D halves, with 16-byte chunk c of row t stored
-// at chunk position c ^ (t & (SW-1)).  The swizzle makes the row-strided MFMA
-// operand reads and the column (transposed) reads of V bank-conflict free.
-template <int D>
+// LDS slot of one tile: 16 rows of D halves; 16-byte chunk c of row t is stored at
+// chunk position c ^ f(t & 15).  The masks were picked by measuring
+// SQ_LDS_BANK_CONFLICT for each access pattern on gfx950:
+//  - K and Q tiles (read as MFMA operands: 16 lanes take one chunk of rows
+//    0..15): f(t) = t, conflict-free;
+//  - V tiles (read transposed by ds_read_b64_tr_b16: chunks 2c, 2c+1 of rows
+//    4q..4q+3 per 16 lanes): f(t) = t ^ 8*(t & 1), conflict-free, where f(t) = t
+//    costs two extra cycles per read.
+// Staging writes (16 consecutive chunks of a row) are conflict-free either way.
+template <int D, bool kIsV = false>
 struct Swz {
   static constexpr int kChunks = D / 8;
-  static constexpr int kSw = kChunks < 16 ? kChunks : 16;
-  static __device__ __forceinline__ int chunk(int row, int c) { return c ^ (row & (kSw - 1)); }
+  static_assert(kChunks >= 16, "the swizzle spans 16 chunk columns");
+  static __device__ __forceinline__ int f(int row) {
+    return kIsV ? (row ^ ((row & 1) << 3)) : row;
+  }
+  static __device__ __forceinline__ int chunk(int row, int c) { return c ^ f(row & 15); }
   static __device__ __forceinline__ int byte_off(int row, int c) {
     return row * (D * 2) + chunk(row, c) * 16;
   }
@@ -206,6 +215,9 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+
+// A value every lane of the wave holds (read from LDS, say), moved to a scalar register.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shfl_xor(x, m, 64)); }
 __device__ __forceinline__ float xor_add(float x, int m) { return x + __shfl_xor(x, m, 64); }
@@ -231,11 +243,16 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& 
   constexpr int DB = D / 16;               // 16-wide head_dim blocks of the PV MFMA
   constexpr int LOADS = D / 32;            // 16-byte loads per lane per tile (K or V)
   constexpr int TILE_BYTES = Phase1Lds<D, W>::kTileBytes;
-  using Z = Swz<D>;
+  using Z = Swz<D>;          // K and Q tiles
+  using ZV = Swz<D, true>;   // V tiles
   static_assert((W - 1) * DB * 64 * 16 + 2 * (W - 1) * 64 * 4 <= W * 2 * TILE_BYTES,
                 "merge area must fit in the tile slots");
 
-  const int lane = threadIdx.x & 63;
+  // The lane index is made opaque to the optimiser here, so the per-lane LDS
+  // addresses derived from it are computed per piece instead of being hoisted
+  // across the balanced kernel's walk, where they would all stay live.
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int Hkv = a.num_kv_heads;
   const int G = a.group;
@@ -300,9 +317,8 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& 
     for (int j = 0; j < LOADS; ++j) {
       const int c = j * 64 + lane;
       const int row = c / Z::kChunks;
-      const int off = Z::byte_off(row, c % Z::kChunks);
-      *reinterpret_cast<u32x4*>(ldsK + off) = rk[j];
-      *reinterpret_cast<u32x4*>(ldsV + off) = rv[j];
+      *reinterpret_cast<u32x4*>(ldsK + Z::byte_off(row, c % Z::kChunks)) = rk[j];
+      *reinterpret_cast<u32x4*>(ldsV + ZV::byte_off(row, c % Z::kChunks)) = rv[j];
     }
     wave_lds_fence();
     // prefetch the wave's next tile while this one is consumed, and the page id of
@@ -363,7 +379,7 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& 
       const int vcol = 16 * c + 4 * (col & 3);
       typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
       const i16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(ldsV + Z::byte_off(vrow, vcol >> 3) + (vcol & 7) * 2));
+          (lds_i16x4*)(ldsV + ZV::byte_off(vrow, vcol >> 3) + (vcol & 7) * 2));
       u32x2 vop = __builtin_bit_cast(u32x2, raw);
       vop.x &= keep_lo;
       vop.y &= keep_hi;
@@ -509,19 +525,20 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(Decod
   if (tid == 0) pre[0] = 0;
   __syncthreads();
 
-  const long long T = pre[S];
-  const long long lo = T * j / NS, hi = T * (j + 1) / NS;
+  // everything below is the same for all lanes: keep it in scalar registers
+  const int T = uniform(pre[S]);
+  const long long lo = (long long)T * j / NS, hi = (long long)T * (j + 1) / NS;
 
   // sequences of length <= 0 get zero rows; spread over the workgroups
   for (int s = w; s < S; s += a.num_wg) {
-    if (pre[s + 1] == pre[s]) {
+    if (uniform(pre[s + 1]) == uniform(pre[s])) {
       uint16_t* o = static_cast<uint16_t*>(a.out) + (size_t)s * a.num_heads * D;
       for (int i = tid; i < a.num_heads * D / 8; i += NT)
         reinterpret_cast<u32x4*>(o)[i] = u32x4{0, 0, 0, 0};
     }
   }
 
-  int2 job = make_int2(-1, 0);
+  int job_q = -1, job_n = 0;
   if (lo == hi) {
     // an empty share (fewer tiles than shares) may lie inside a sequence that
     // neighbouring shares split: leave the identity (-inf, 0) in slot 0
@@ -532,29 +549,31 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(Decod
     int s = 0, top = S - 1;
     while (s < top) {
       const int mid = (s + top + 1) >> 1;
-      if (pre[mid] <= lo) s = mid; else top = mid - 1;
+      if (uniform(pre[mid]) <= lo) s = mid; else top = mid - 1;
     }
-    long long x = lo;
-    while (x < hi) {
-      const long long seg0 = pre[s], seg1 = pre[s + 1];
-      const int n = static_cast<int>(seg1 - seg0);
-      const int ta = static_cast<int>(x - seg0);
-      const int tb = static_cast<int>(min(hi, seg1) - seg0);
+    int x = static_cast<int>(lo);
+    const int x_end = static_cast<int>(hi);
+    while (x < x_end) {
+      const int seg0 = uniform(pre[s]), seg1 = uniform(pre[s + 1]);
+      const int n = seg1 - seg0;
+      const int ta = x - seg0;
+      const int tb = min(x_end, seg1) - seg0;
       const bool final = ta == 0 && tb == n;
       const long long rec = 2LL * w + (ta > 0 ? 0 : 1);
       if (ta == 0 && !final) {
         // this share starts a sequence that later shares continue: it owns the merge
-        const long long last = (seg1 * NS - 1) / T;      // share holding tile seg1-1
-        job = make_int2(s * Hkv + kvh, static_cast<int>(last - j + 1));
+        const long long last = ((long long)seg1 * NS - 1) / T;   // share holding tile seg1-1
+        job_q = s * Hkv + kvh;
+        job_n = static_cast<int>(last - j + 1);
       }
       // the piece ends at its last tile, or at the sequence's last token
-      const int t_end = tb == n ? kTile * (n - 1) + last_len[s] : kTile * tb;
+      const int t_end = tb == n ? kTile * (n - 1) + uniform(last_len[s]) : kTile * tb;
       run_piece<D, DT, W>(a, sm, s, kvh, kTile * ta, t_end, final, rec);
-      x = seg1 < hi ? seg1 : hi;
-      do { ++s; } while (s < S && pre[s + 1] == pre[s] && x < hi);
+      x = min(seg1, x_end);
+      do { ++s; } while (s < S && uniform(pre[s + 1]) == uniform(pre[s]) && x < x_end);
     }
   }
-  if (tid == 0) a.jobs[w] = job;
+  if (tid == 0) a.jobs[w] = make_int2(job_q, job_n);
 }
 
 // ---------------------------------------------------------------------------
