@@ -109,6 +109,8 @@ def main():
     ap.add_argument("--p512", action="store_true",
                     help="also time the pages' fixed 512-token partitions (context only)")
     ap.add_argument("--single-pass-max-len", type=int, default=None)
+    ap.add_argument("--per-query-head", action="store_true",
+                    help="ablation: one workgroup per query head (KV read once per query head)")
     ap.add_argument("--no-hint", action="store_true",
                     help="do not pass the host-side total of seq_lens to the planner")
     ap.add_argument("--num-cus", type=int, default=0,
@@ -144,7 +146,8 @@ def main():
         return pa.Decoder(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size,
                           w.max_blocks_per_seq, w.q.dtype, max_seq_len=w.max_seq_len,
                           partition_size=P, single_pass_max_len=args.single_pass_max_len,
-                          num_cus=args.num_cus, total_tokens_hint=total)
+                          num_cus=args.num_cus, total_tokens_hint=total,
+                          per_query_head=args.per_query_head)
 
     P = args.partition_size
     # the caller knows its sequence lengths on the host: pass their sum
@@ -153,7 +156,7 @@ def main():
     info = pa.plan(list(w.seq_lens_host), w.num_heads, w.num_kv_heads, w.head_dim,
                    w.block_size, w.max_blocks_per_seq, w.max_seq_len, P,
                    single_pass_max_len=args.single_pass_max_len, num_cus=args.num_cus,
-                   total_tokens_hint=total)
+                   total_tokens_hint=total, per_query_head=args.per_query_head)
     log(f"plan: {info}")
 
     if args.copy_probe_mib > 0:
@@ -250,6 +253,7 @@ def main():
                    "partition_size_arg": P,
                    "single_pass_max_len": info["single_pass_max_len"],
                    "split": "balanced" if info["balanced"] else "fixed partitions",
+                   "grid": "per query head (ablation)" if args.per_query_head else "per KV head",
                    "kv_bytes_per_step": kv, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "pa_phase1_kernel",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -25,7 +25,8 @@ SYMBOLS = ("paged_attn_workspace_size", "paged_attn_workspace_size_ex", "paged_a
 
 class Options(ctypes.Structure):
     _fields_ = [("single_pass_max_len", ctypes.c_int), ("num_cus", ctypes.c_int),
-                ("total_tokens_hint", ctypes.c_longlong), ("reserved", ctypes.c_int * 4),
+                ("total_tokens_hint", ctypes.c_longlong), ("per_query_head", ctypes.c_int),
+                ("reserved", ctypes.c_int * 3),
                 ("phase1_begin", ctypes.c_void_p), ("phase1_end", ctypes.c_void_p)]
 
 
@@ -87,8 +88,10 @@ def _check(status: int):
 
 
 def _opts(single_pass_max_len: Optional[int], num_cus: int = 0,
-          events: Optional[Tuple[int, int]] = None, total_tokens_hint: int = 0) -> Options:
+          events: Optional[Tuple[int, int]] = None, total_tokens_hint: int = 0,
+          per_query_head: bool = False) -> Options:
     o = Options()
+    o.per_query_head = 1 if per_query_head else 0
     o.single_pass_max_len = -1 if single_pass_max_len is None else int(single_pass_max_len)
     o.num_cus = int(num_cus)
     o.total_tokens_hint = int(total_tokens_hint)
@@ -104,7 +107,8 @@ def _ptr(t: Optional[torch.Tensor]):
 def plan(seq_lens_host, num_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
          max_blocks_per_seq: int, max_seq_len: int = 0, partition_size: int = 0,
          dtype: int = PA_F16, single_pass_max_len: Optional[int] = None,
-         num_seqs: Optional[int] = None, num_cus: int = 0, total_tokens_hint: int = 0) -> dict:
+         num_seqs: Optional[int] = None, num_cus: int = 0, total_tokens_hint: int = 0,
+         per_query_head: bool = False) -> dict:
     """Host-only plan (no GPU needed).  seq_lens_host: sequence of ints or None."""
     arr = None
     if seq_lens_host is not None:
@@ -112,7 +116,8 @@ def plan(seq_lens_host, num_heads: int, num_kv_heads: int, head_dim: int, block_
         arr = (ctypes.c_int32 * n)(*[int(x) for x in seq_lens_host])
         num_seqs = n
     info = PlanInfo()
-    o = _opts(single_pass_max_len, num_cus, total_tokens_hint=total_tokens_hint)
+    o = _opts(single_pass_max_len, num_cus, total_tokens_hint=total_tokens_hint,
+              per_query_head=per_query_head)
     _check(lib().paged_attn_plan(arr, int(num_seqs or 0), num_heads, num_kv_heads, head_dim,
                                  block_size, max_blocks_per_seq, max_seq_len, partition_size,
                                  dtype, ctypes.byref(o), ctypes.byref(info)))
@@ -122,8 +127,10 @@ def plan(seq_lens_host, num_heads: int, num_kv_heads: int, head_dim: int, block_
 def workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
                    block_size: int, max_blocks_per_seq: int, max_seq_len: int = 0,
                    partition_size: int = 0, single_pass_max_len: Optional[int] = None,
-                   total_tokens_hint: int = 0, num_cus: int = 0) -> int:
-    o = _opts(single_pass_max_len, num_cus, total_tokens_hint=total_tokens_hint)
+                   total_tokens_hint: int = 0, num_cus: int = 0,
+                   per_query_head: bool = False) -> int:
+    o = _opts(single_pass_max_len, num_cus, total_tokens_hint=total_tokens_hint,
+              per_query_head=per_query_head)
     n = lib().paged_attn_workspace_size_ex(num_seqs, num_heads, num_kv_heads, head_dim,
                                            block_size, max_blocks_per_seq, max_seq_len,
                                            partition_size, ctypes.byref(o))
@@ -143,16 +150,18 @@ class Decoder:
                  block_size: int, max_blocks_per_seq: int, dtype: torch.dtype,
                  max_seq_len: int = 0, partition_size: int = 0,
                  single_pass_max_len: Optional[int] = None, total_tokens_hint: int = 0,
-                 num_cus: int = 0, device="cuda"):
+                 num_cus: int = 0, per_query_head: bool = False, device="cuda"):
         self.shape = (num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                       max_blocks_per_seq)
         self.dtype = dtype
         self.max_seq_len = int(max_seq_len)
         self.partition_size = int(partition_size)
-        self.opts = _opts(single_pass_max_len, num_cus, total_tokens_hint=total_tokens_hint)
+        self.opts = _opts(single_pass_max_len, num_cus, total_tokens_hint=total_tokens_hint,
+                          per_query_head=per_query_head)
         nbytes = workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                                 max_blocks_per_seq, max_seq_len, partition_size,
-                                single_pass_max_len, total_tokens_hint, num_cus)
+                                single_pass_max_len, total_tokens_hint, num_cus,
+                                per_query_head)
         self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
         self.workspace_bytes = nbytes
         self.out = torch.empty((num_seqs, num_heads, head_dim), dtype=dtype, device=device)
@@ -195,19 +204,21 @@ def decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
            block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
            partition_size: int = 0, max_seq_len: int = 0, out: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None, single_pass_max_len: Optional[int] = None,
-           events: Optional[Tuple[int, int]] = None, total_tokens_hint: int = 0) -> torch.Tensor:
+           events: Optional[Tuple[int, int]] = None, total_tokens_hint: int = 0,
+           per_query_head: bool = False) -> torch.Tensor:
     """One decode step: out[s,h] = softmax(scale q K^T) V over the paged caches."""
     _validate(q, key_cache, value_cache, block_tables, seq_lens)
     S, Hq, D = q.shape
     _, Hkv, bs, _ = key_cache.shape
     mbps = block_tables.shape[1]
     need = workspace_size(S, Hq, Hkv, D, bs, mbps, max_seq_len, partition_size,
-                          single_pass_max_len, total_tokens_hint)
+                          single_pass_max_len, total_tokens_hint, 0, per_query_head)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty_like(q)
-    o = _opts(single_pass_max_len, events=events, total_tokens_hint=total_tokens_hint)
+    o = _opts(single_pass_max_len, events=events, total_tokens_hint=total_tokens_hint,
+              per_query_head=per_query_head)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(lib().paged_attn_decode_ex(
         _ptr(out), _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),

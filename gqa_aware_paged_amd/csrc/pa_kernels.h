@@ -97,7 +97,9 @@ struct BF16 {
 // head, the normalised output of a piece (fp32) and (max in base 2, exp sum).
 // ws_acc is [D/16][R][G][16] floats (slice-major: phase 2 reads the records of
 // one 16-wide slice back to back) and ws_ml is [R][G] float2.
-//  - grid mode:     record (s*Hkv + kvh)*max_parts + partition, R = S*Hkv*max_parts
+//  - grid mode:     record (s*units + unit)*max_parts + partition,
+//                   R = S*units*max_parts (units = Hkv, or Hq in the per-query-head
+//                   ablation)
 //  - balanced mode: record 2*w + slot of workgroup w (slot 0: the piece that
 //                   ends a sequence begun in an earlier share, slot 1: the piece
 //                   that begins a sequence continued in a later share), R = 2*num_wg
@@ -115,7 +117,9 @@ struct DecodeArgs {
   int num_seqs;
   int num_heads;
   int num_kv_heads;
-  int group;
+  int group;                // query heads one workgroup serves (a "head unit")
+  int units;                // head units per sequence (num_heads / group)
+  int kv_group;             // query heads per KV head (num_heads / num_kv_heads)
   int block_size;
   int max_blocks_per_seq;
   int max_seq_len;          // lengths are clamped to this bound
@@ -237,7 +241,7 @@ struct Phase1Lds {
 // barrier, so LDS from a previous piece may be reused.
 template <int D, class DT, int W>
 __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& sm, int s,
-                                          int kvh, int t_begin, int t_end, bool final,
+                                          int unit, int t_begin, int t_end, bool final,
                                           long long rec) {
   constexpr int KS = D / 32;               // k-steps of the QK^T MFMA (32 dims each)
   constexpr int DB = D / 16;               // 16-wide head_dim blocks of the PV MFMA
@@ -257,6 +261,7 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& 
   const int Hkv = a.num_kv_heads;
   const int G = a.group;
   const int Hq = a.num_heads;
+  const int kvh = unit * G / a.kv_group;   // KV head read by the unit's query heads
   const int col = lane & 15;     // query head (QK^T/PV columns) or row index within a tile
   const int grp = lane >> 4;     // 4-lane-group index: k-slot block / 4-row block
 
@@ -267,7 +272,7 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& 
   constexpr int QLOADS = (kTile * D / 8 + W * 64 - 1) / (W * 64);
   u32x4 qv[QLOADS];
   {
-    const uint16_t* qg = a.q + ((size_t)s * Hq + (size_t)kvh * G) * D;
+    const uint16_t* qg = a.q + ((size_t)s * Hq + (size_t)unit * G) * D;
 #pragma unroll
     for (int j = 0; j < QLOADS; ++j) {
       const int i = threadIdx.x + j * W * 64;
@@ -290,7 +295,7 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& 
   }
 
   // Q of the group in LDS as the B operand of S^T = K Q^T: row h is query head
-  // kvh*G + h (rows G..15 are zero), swizzled like a K tile.
+  // unit*G + h (rows G..15 are zero), swizzled like a K tile.
   __syncthreads();                 // LDS of a previous piece may still be read
 #pragma unroll
   for (int j = 0; j < QLOADS; ++j) {
@@ -423,7 +428,7 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& 
     if (col < G) {
       const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
       if (final) {
-        uint16_t* o = static_cast<uint16_t*>(a.out) + ((size_t)s * Hq + kvh * G + col) * D +
+        uint16_t* o = static_cast<uint16_t*>(a.out) + ((size_t)s * Hq + unit * G + col) * D +
                       4 * grp;
 #pragma unroll
         for (int c = 0; c < DB; ++c) {
@@ -448,8 +453,8 @@ template <int D, class DT, int W>
 __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) Phase1Lds<D, W> sm;
   int wg = blockIdx.x;
-  const int kvh = wg % a.num_kv_heads;
-  wg /= a.num_kv_heads;
+  const int unit = wg % a.units;
+  wg /= a.units;
   const int s = wg % a.num_seqs;
   const int part = wg / a.num_seqs;
   const int L = clamp_len(a, s);
@@ -465,8 +470,8 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_kernel(DecodeArgs a) 
     t_begin = part * a.partition_size;
     t_end = min(L, t_begin + a.partition_size);
   }
-  const long long rec = ((long long)s * a.num_kv_heads + kvh) * a.max_parts + part;
-  run_piece<D, DT, W>(a, sm, s, kvh, t_begin, t_end, single, rec);
+  const long long rec = ((long long)s * a.units + unit) * a.max_parts + part;
+  run_piece<D, DT, W>(a, sm, s, unit, t_begin, t_end, single, rec);
 }
 
 // Balanced mode.  Sequence s has n(s) = ceil(L_s/16) tiles per KV head; laid end
@@ -623,28 +628,28 @@ __global__ __launch_bounds__(kRedThreads) void pa_reduce_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Hkv = a.num_kv_heads, Hq = a.num_heads;
   const int sg = blockIdx.x % NSG;
-  const int unit = blockIdx.x / NSG;
+  const int slot = blockIdx.x / NSG;       // segment (grid mode) or phase-1 workgroup
 
   int q, np;
   long long rec0, step, first;
   if constexpr (BAL) {
-    const int2 job = a.jobs[unit];
+    const int2 job = a.jobs[slot];
     if (job.x < 0) return;
     q = job.x;
     np = job.y;
-    rec0 = 2LL * unit;
+    rec0 = 2LL * slot;
     step = 2LL * Hkv;
     first = 1;
   } else {
-    q = unit;
-    const int L = clamp_len(a, q / Hkv);
+    q = slot;
+    const int L = clamp_len(a, q / a.units);
     if (L <= a.single_pass_max_len) return;     // served in one pass by phase 1
     np = (L + a.partition_size - 1) / a.partition_size;
     rec0 = (long long)q * a.max_parts;
     step = 1;
     first = 0;
   }
-  const int s = q / Hkv, kvh = q % Hkv;
+  const int s = q / a.units, unit = q % a.units;   // balanced mode: units == Hkv
   const long long R = a.records;
 
   const int ql = tid % QL;
@@ -705,7 +710,7 @@ __global__ __launch_bounds__(kRedThreads) void pa_reduce_kernel(DecodeArgs a) {
 #pragma unroll
     for (int w = 1; w < kRedWaves; ++w) combine_into(t, red_m[w][h][qq], red_w[w][h][qq], red_a[w][h][qq]);
     const f32x4 y = t.a * (1.f / t.w);
-    uint16_t* o = static_cast<uint16_t*>(a.out) + ((size_t)s * Hq + kvh * G + h) * D +
+    uint16_t* o = static_cast<uint16_t*>(a.out) + ((size_t)s * Hq + unit * G + h) * D +
                   sg * SPW * 16 + 4 * qq;
     const u32x2 packed = {DT::bits(y[0]) | (DT::bits(y[1]) << 16),
                           DT::bits(y[2]) | (DT::bits(y[3]) << 16)};

@@ -39,7 +39,8 @@ struct Plan {
   int T1 = 0;            // single-pass threshold (tokens), grid mode
   int max_parts = 0;     // partitions per (seq, kv head) slot; 0 = no phase 2, grid mode
   int max_seq_len = 0;   // resolved length bound
-  int group = 0;
+  int group = 0;         // query heads per workgroup
+  int units = 0;         // head units per sequence (num_kv_heads, or num_heads)
   int num_wg = 0;        // phase-1 workgroups, balanced mode
   long long records = 0; // partial records in the workspace
   long long grid1 = 0, grid2 = 0;
@@ -84,7 +85,11 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int P_req,
               const pa_options* opt, Plan& pl) {
   pl = Plan{};
-  pl.group = Hq / Hkv;
+  // per-query-head ablation: one workgroup per query head (each KV page is then
+  // read once per query head instead of once per KV head)
+  const bool per_qhead = opt && opt->per_query_head;
+  pl.units = per_qhead ? Hq : Hkv;
+  pl.group = Hq / pl.units;
   pl.max_seq_len = max_len > 0 ? max_len : mbps * bs;
   const int cus = (opt && opt->num_cus > 0) ? opt->num_cus : kDefaultCUs;
   const bool forced_tier = opt && opt->single_pass_max_len >= 0;
@@ -93,7 +98,8 @@ int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int 
   // and need no device-side prefix of seq_lens
   const long long hint = opt ? opt->total_tokens_hint : 0;
   const bool uniform = hint > 0 && hint == static_cast<long long>(S) * pl.max_seq_len;
-  pl.balanced = P_req == 0 && !forced_tier && !uniform && S <= pa::kMaxBalancedSeqs;
+  pl.balanced = P_req == 0 && !forced_tier && !uniform && !per_qhead &&
+                S <= pa::kMaxBalancedSeqs;
   if (pl.balanced) {
     // shares x KV heads: about two resident workgroups per CU, but at least
     // kMinTilesPerWG tiles per workgroup
@@ -108,14 +114,14 @@ int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int 
     pl.grid2 = static_cast<long long>(pl.num_wg) * (D / 16 / kBalancedSlices);
     pl.T1 = -1;
   } else {
-    pl.P = P_req > 0 ? P_req : auto_partition(S, Hkv, pl.max_seq_len, cus, hint);
+    pl.P = P_req > 0 ? P_req : auto_partition(S, pl.units, pl.max_seq_len, cus, hint);
     // a sequence that fits in one partition is served in one pass
     pl.T1 = forced_tier ? opt->single_pass_max_len : pl.P;
     if (pl.max_seq_len > pl.T1) pl.max_parts = (pl.max_seq_len + pl.P - 1) / pl.P;
     const long long parts = pl.max_parts > 0 ? pl.max_parts : 1;
-    pl.grid1 = static_cast<long long>(S) * Hkv * parts;
-    pl.grid2 = pl.max_parts > 0 ? static_cast<long long>(S) * Hkv * (D / 16) : 0;
-    pl.records = static_cast<long long>(S) * Hkv * pl.max_parts;
+    pl.grid1 = static_cast<long long>(S) * pl.units * parts;
+    pl.grid2 = pl.max_parts > 0 ? static_cast<long long>(S) * pl.units * (D / 16) : 0;
+    pl.records = static_cast<long long>(S) * pl.units * pl.max_parts;
   }
   if (pl.grid1 > std::numeric_limits<int>::max() || pl.grid2 > std::numeric_limits<int>::max())
     return PA_ERR_SHAPE;
@@ -337,6 +343,8 @@ PA_API int paged_attn_decode_ex(void* out, const void* q, const void* key_cache,
   args.num_heads = num_heads;
   args.num_kv_heads = num_kv_heads;
   args.group = pl.group;
+  args.units = pl.units;
+  args.kv_group = num_heads / num_kv_heads;
   args.block_size = block_size;
   args.max_blocks_per_seq = max_blocks_per_seq;
   args.max_seq_len = pl.max_seq_len;

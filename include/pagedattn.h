@@ -98,7 +98,11 @@ typedef struct pa_options {
      * instead of the device-side balanced split; with a forced tier it sizes the
      * automatic partitions. */
     long long total_tokens_hint;
-    int reserved[4];
+    /* Ablation only: 1 launches one workgroup per query head instead of one per
+     * KV head (the GQA-unaware grid; each KV page is read once per query head).
+     * Uses fixed partitions (partition_size, or 0 for one workgroup per CU). */
+    int per_query_head;
+    int reserved[3];
     /* If non-NULL, hipEventRecord(phase1_begin/phase1_end, stream) is issued
      * immediately before/after the phase-1 kernel (instrumentation only). */
     hipEvent_t phase1_begin;

@@ -114,6 +114,11 @@ def test_plan_matches_pages_grid(lib):
     assert info["group"] == g["gqa_ratio"] == g["kv_reads_saved_factor"]
     assert info["active_workgroups"] == 800
     assert info["partitioned_seqs"] == 1
+    # the per-query-head ablation restores the pages' "before" grid
+    info_q = pa.plan([L], g["num_q_heads"], g["num_kv_heads"], g["tile_head_dim"], 16,
+                     L // 16, L, P, single_pass_max_len=0, per_query_head=True)
+    assert info_q["phase1_workgroups"] == g["blocks_per_q_head_grid"]
+    assert info_q["group"] == 1 and info_q["workspace_bytes"] == info["workspace_bytes"]
     # the same arithmetic for the 4-sequence long-context workload
     info4 = pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, P)
     assert info4["phase1_workgroups"] == 3200 and info4["phase2_workgroups"] == 4 * 4 * 16

@@ -284,6 +284,23 @@ def test_needle_high_page_ids():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("P", [256, 1024, 0])
+def test_per_query_head_ablation(P):
+    """One workgroup per query head computes each head's column exactly as the
+    grouped workgroup does: with the same partitions the outputs agree bit for bit.
+    (P = 0 sizes partitions per head unit, so only the oracle check applies.)"""
+    say(f"case per-query-head ablation P={P}")
+    w = make([1, 100, 700, 2000], partition_size=256)
+    ablation = pa.decode(w.q, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, w.scale,
+                         partition_size=P, max_seq_len=w.max_seq_len, single_pass_max_len=0,
+                         per_query_head=True)
+    if P:
+        grouped = run(w, 0, P=P)
+        torch.cuda.synchronize()
+        assert torch.equal(grouped, ablation)
+    assert_close(gpu_out(ablation), oracle_full(w), "per-query-head")
+
+
 def test_workspace_reuse_and_stream():
     """A Decoder reuses one caller-owned workspace across calls and runs on a side stream."""
     say("case workspace reuse")
