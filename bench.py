@@ -111,6 +111,8 @@ def main():
     ap.add_argument("--single-pass-max-len", type=int, default=None)
     ap.add_argument("--per-query-head", action="store_true",
                     help="ablation: one workgroup per query head (KV read once per query head)")
+    ap.add_argument("--fused", action="store_true",
+                    help="merge partitions inside phase 1 (atomic ticket) instead of a phase-2 launch")
     ap.add_argument("--no-hint", action="store_true",
                     help="do not pass the host-side total of seq_lens to the planner")
     ap.add_argument("--num-cus", type=int, default=0,
@@ -147,7 +149,7 @@ def main():
                           w.max_blocks_per_seq, w.q.dtype, max_seq_len=w.max_seq_len,
                           partition_size=P, single_pass_max_len=args.single_pass_max_len,
                           num_cus=args.num_cus, total_tokens_hint=total,
-                          per_query_head=args.per_query_head)
+                          per_query_head=args.per_query_head, fused_combine=args.fused)
 
     P = args.partition_size
     # the caller knows its sequence lengths on the host: pass their sum
@@ -156,7 +158,8 @@ def main():
     info = pa.plan(list(w.seq_lens_host), w.num_heads, w.num_kv_heads, w.head_dim,
                    w.block_size, w.max_blocks_per_seq, w.max_seq_len, P,
                    single_pass_max_len=args.single_pass_max_len, num_cus=args.num_cus,
-                   total_tokens_hint=total, per_query_head=args.per_query_head)
+                   total_tokens_hint=total, per_query_head=args.per_query_head,
+                   fused_combine=args.fused)
     log(f"plan: {info}")
 
     if args.copy_probe_mib > 0:
@@ -254,8 +257,11 @@ def main():
                    "single_pass_max_len": info["single_pass_max_len"],
                    "split": "balanced" if info["balanced"] else "fixed partitions",
                    "grid": "per query head (ablation)" if args.per_query_head else "per KV head",
+                   "combine": "fused in phase 1" if info["fused"] else
+                   ("phase-2 kernel" if info["phase2_workgroups"] else "none (one pass)"),
                    "kv_bytes_per_step": kv, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "pa_phase1_kernel",
+        "roofline": {"bound": "hbm",
+                     "kernel": "pa_phase1_balanced_kernel" if info["balanced"] else "pa_phase1_kernel",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_counters(kv) if args.workload == "long" else None,

@@ -20,13 +20,13 @@ PA_F16, PA_BF16 = 0, 1
 _DTYPE = {torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 SYMBOLS = ("paged_attn_workspace_size", "paged_attn_workspace_size_ex", "paged_attn_decode",
            "paged_attn_decode_ex", "paged_attn_status_str", "paged_attn_plan",
-           "paged_attn_gather_probe")
+           "paged_attn_gather_probe", "paged_attn_workspace_init")
 
 
 class Options(ctypes.Structure):
     _fields_ = [("single_pass_max_len", ctypes.c_int), ("num_cus", ctypes.c_int),
                 ("total_tokens_hint", ctypes.c_longlong), ("per_query_head", ctypes.c_int),
-                ("reserved", ctypes.c_int * 3),
+                ("fused_combine", ctypes.c_int), ("reserved", ctypes.c_int * 2),
                 ("phase1_begin", ctypes.c_void_p), ("phase1_end", ctypes.c_void_p)]
 
 
@@ -38,7 +38,7 @@ class PlanInfo(ctypes.Structure):
                 ("active_workgroups", ctypes.c_longlong), ("single_pass_seqs", ctypes.c_int),
                 ("partitioned_seqs", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t),
                 ("threads_per_workgroup", ctypes.c_int), ("lds_bytes_phase1", ctypes.c_int),
-                ("balanced", ctypes.c_int)]
+                ("balanced", ctypes.c_int), ("fused", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_plan.restype = I
         L.paged_attn_gather_probe.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P]
         L.paged_attn_gather_probe.restype = I
+        L.paged_attn_workspace_init.argtypes = [P, Z, P]
+        L.paged_attn_workspace_init.restype = I
         _lib = L
     return _lib
 
@@ -89,9 +91,10 @@ def _check(status: int):
 
 def _opts(single_pass_max_len: Optional[int], num_cus: int = 0,
           events: Optional[Tuple[int, int]] = None, total_tokens_hint: int = 0,
-          per_query_head: bool = False) -> Options:
+          per_query_head: bool = False, fused_combine: bool = False) -> Options:
     o = Options()
     o.per_query_head = 1 if per_query_head else 0
+    o.fused_combine = 1 if fused_combine else 0
     o.single_pass_max_len = -1 if single_pass_max_len is None else int(single_pass_max_len)
     o.num_cus = int(num_cus)
     o.total_tokens_hint = int(total_tokens_hint)
@@ -108,7 +111,7 @@ def plan(seq_lens_host, num_heads: int, num_kv_heads: int, head_dim: int, block_
          max_blocks_per_seq: int, max_seq_len: int = 0, partition_size: int = 0,
          dtype: int = PA_F16, single_pass_max_len: Optional[int] = None,
          num_seqs: Optional[int] = None, num_cus: int = 0, total_tokens_hint: int = 0,
-         per_query_head: bool = False) -> dict:
+         per_query_head: bool = False, fused_combine: bool = False) -> dict:
     """Host-only plan (no GPU needed).  seq_lens_host: sequence of ints or None."""
     arr = None
     if seq_lens_host is not None:
@@ -117,7 +120,7 @@ def plan(seq_lens_host, num_heads: int, num_kv_heads: int, head_dim: int, block_
         num_seqs = n
     info = PlanInfo()
     o = _opts(single_pass_max_len, num_cus, total_tokens_hint=total_tokens_hint,
-              per_query_head=per_query_head)
+              per_query_head=per_query_head, fused_combine=fused_combine)
     _check(lib().paged_attn_plan(arr, int(num_seqs or 0), num_heads, num_kv_heads, head_dim,
                                  block_size, max_blocks_per_seq, max_seq_len, partition_size,
                                  dtype, ctypes.byref(o), ctypes.byref(info)))
@@ -139,31 +142,45 @@ def workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: i
     return int(n)
 
 
+def workspace_init(workspace: torch.Tensor, stream: Optional[int] = None) -> None:
+    """Clear the ticket area of a workspace for the fused combine (enqueued on
+    `stream`, default the current stream)."""
+    if stream is None:
+        stream = torch.cuda.current_stream(workspace.device).cuda_stream
+    _check(lib().paged_attn_workspace_init(_ptr(workspace),
+                                           workspace.numel() * workspace.element_size(),
+                                           ctypes.c_void_p(stream)))
+
+
 class Decoder:
     """Holds the workspace of one decode configuration so the hot call allocates nothing.
 
     Mirrors the caller-owned workspace of the C ABI: allocate once, then call
-    `__call__` every step.
+    `__call__` every step.  With fused_combine the workspace's ticket area is
+    cleared once here; every completed call leaves it clear.
     """
 
     def __init__(self, num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
                  block_size: int, max_blocks_per_seq: int, dtype: torch.dtype,
                  max_seq_len: int = 0, partition_size: int = 0,
                  single_pass_max_len: Optional[int] = None, total_tokens_hint: int = 0,
-                 num_cus: int = 0, per_query_head: bool = False, device="cuda"):
+                 num_cus: int = 0, per_query_head: bool = False,
+                 fused_combine: bool = False, device="cuda"):
         self.shape = (num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                       max_blocks_per_seq)
         self.dtype = dtype
         self.max_seq_len = int(max_seq_len)
         self.partition_size = int(partition_size)
         self.opts = _opts(single_pass_max_len, num_cus, total_tokens_hint=total_tokens_hint,
-                          per_query_head=per_query_head)
+                          per_query_head=per_query_head, fused_combine=fused_combine)
         nbytes = workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                                 max_blocks_per_seq, max_seq_len, partition_size,
                                 single_pass_max_len, total_tokens_hint, num_cus,
                                 per_query_head)
         self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
         self.workspace_bytes = nbytes
+        if fused_combine and nbytes > 0:
+            workspace_init(self.workspace)
         self.out = torch.empty((num_seqs, num_heads, head_dim), dtype=dtype, device=device)
 
     def __call__(self, q, key_cache, value_cache, block_tables, seq_lens, scale: float,
@@ -205,8 +222,11 @@ def decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
            partition_size: int = 0, max_seq_len: int = 0, out: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None, single_pass_max_len: Optional[int] = None,
            events: Optional[Tuple[int, int]] = None, total_tokens_hint: int = 0,
-           per_query_head: bool = False) -> torch.Tensor:
-    """One decode step: out[s,h] = softmax(scale q K^T) V over the paged caches."""
+           per_query_head: bool = False, fused_combine: bool = False) -> torch.Tensor:
+    """One decode step: out[s,h] = softmax(scale q K^T) V over the paged caches.
+
+    fused_combine: merge partitions inside phase 1; a workspace passed in must then
+    have a clear ticket area (workspace_init, or a previous fused call)."""
     _validate(q, key_cache, value_cache, block_tables, seq_lens)
     S, Hq, D = q.shape
     _, Hkv, bs, _ = key_cache.shape
@@ -215,10 +235,12 @@ def decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
                           single_pass_max_len, total_tokens_hint, 0, per_query_head)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if fused_combine:
+            workspace_init(workspace)
     if out is None:
         out = torch.empty_like(q)
     o = _opts(single_pass_max_len, events=events, total_tokens_hint=total_tokens_hint,
-              per_query_head=per_query_head)
+              per_query_head=per_query_head, fused_combine=fused_combine)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(lib().paged_attn_decode_ex(
         _ptr(out), _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),

@@ -33,6 +33,12 @@
 // with the rescale of the online-softmax fix (page of commit 87a19d2): with M
 // the largest max, partial p weighs l_p 2^(m_p - M) and the output is
 // sum_p weight_p acc_p / sum_p weight_p, evaluated as an associative fold.
+//
+// Fused combine (the cross-partition "Level 3" of the pages' three-level
+// decomposition, done inside phase 1): every workgroup that writes a partial
+// takes a device-scope ticket for its segment after releasing the record; the
+// one that draws the last ticket merges the segment's records with the same fold
+// and writes the output, then resets the ticket to zero.  No second launch.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -113,6 +119,7 @@ struct DecodeArgs {
   float* ws_acc;
   float2* ws_ml;
   int2* jobs;               // balanced mode: [num_wg] (segment, partial count) or (-1, 0)
+  unsigned* tickets;        // fused combine: one counter per segment, zero between calls; else null
   long long records;        // R
   int num_seqs;
   int num_heads;
@@ -226,6 +233,56 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 __device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shfl_xor(x, m, 64)); }
 __device__ __forceinline__ float xor_add(float x, int m) { return x + __shfl_xor(x, m, 64); }
 
+// Merge of two compound partials (m, w, a): m is a base-2 max, w the weight sum
+// and a the weighted sum, both relative to m.  (-inf, 0, 0) is the identity.
+struct Partial {
+  float m, w;
+  f32x4 a;
+};
+
+__device__ __forceinline__ void combine_into(Partial& x, float om, float ow, f32x4 oa) {
+  const float nm = fmaxf(x.m, om);
+  const float fx = nm == kNegInf ? 0.f : __builtin_amdgcn_exp2f(x.m - nm);
+  const float fo = nm == kNegInf ? 0.f : __builtin_amdgcn_exp2f(om - nm);
+  x.w = x.w * fx + ow * fo;
+  x.a = x.a * fx + oa * fo;
+  x.m = nm;
+}
+
+// Device-scope accesses for the fused combine.  Records cross XCDs, each with its
+// own L2: they are written with device-scope stores (write-through to the
+// device's point of coherence) and read back with device-scope loads, so no
+// L2 write-back or invalidate (which would serialise every finishing workgroup
+// of an XCD) is needed.  64-bit accesses, two per float4.
+typedef unsigned long long u64;
+
+__device__ __forceinline__ void store_dev(float* p, f32x4 v) {
+  const u32x4 b = __builtin_bit_cast(u32x4, v);
+  u64* q = reinterpret_cast<u64*>(p);
+  __hip_atomic_store(q, (u64)b.x | ((u64)b.y << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, (u64)b.z | ((u64)b.w << 32), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_dev(float2* p, float2 v) {
+  __hip_atomic_store(reinterpret_cast<u64*>(p), __builtin_bit_cast(u64, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ f32x4 load_dev(const float* p) {
+  const u64* q = reinterpret_cast<const u64*>(p);
+  const u64 lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const u64 hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_bit_cast(f32x4, u32x4{(unsigned)lo, (unsigned)(lo >> 32), (unsigned)hi,
+                                         (unsigned)(hi >> 32)});
+}
+
+__device__ __forceinline__ float2 load_dev(const float2* p) {
+  return __builtin_bit_cast(
+      float2, __hip_atomic_load(reinterpret_cast<const u64*>(p), __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT));
+}
+
 // ---------------------------------------------------------------------------
 // Phase 1: one piece = tokens [t_begin, t_end) of segment (s, kvh).
 // ---------------------------------------------------------------------------
@@ -234,15 +291,138 @@ struct Phase1Lds {
   static constexpr int kTileBytes = kTile * D * 2;
   unsigned char tiles[W * 2 * kTileBytes];   // per wave: K tile, V tile; merge area at the end
   unsigned char q[kTileBytes];               // the group's Q rows (16 rows, zero-padded)
+  int last;                                  // fused combine: this workgroup drew the last ticket
 };
 
+// The records a segment's partials went to, for the fused combine: partial p
+// (0 <= p < np) is record rec0 + step*p, plus `first` for p = 0.  seg < 0: the
+// piece is not a partial.
+struct SegMerge {
+  int seg;
+  int np;
+  long long rec0, step, first;
+};
+
+// Fused combine, run by the workgroup that drew a segment's last ticket: merges
+// the np records of segment (s, unit) into its G output rows.  Wave w takes the
+// heads w, w + W, ...; within a wave, lane covers head_dim values 4*(lane % QL)
+// .. +3 (QL = D/4) and, when a head row is narrower than the wave, the LPW lane
+// groups fold alternate partials and are combined by shuffles.  Each round keeps
+// U partials of every head of the wave in flight.  Same arithmetic as
+// pa_reduce_kernel.
+template <int D, class DT, int G, int W>
+__device__ __forceinline__ void merge_records(const DecodeArgs& a, int s, int unit,
+                                              const SegMerge& mg) {
+  constexpr int QL = D / 4;                 // float4 lanes per head row
+  constexpr int LPW = 64 / QL;              // lane groups per wave
+  constexpr int HPW = (G + W - 1) / W;      // heads per wave (at most)
+  constexpr int U = 16 / HPW;               // partials per round and lane group
+  static_assert(QL <= 64 && 64 % QL == 0, "a head row must tile a wave");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ql = lane % QL;
+  const int lg = lane / QL;
+  const int slice = ql / 4, q4 = ql % 4;
+  const long long R = a.records;
+  const int np = mg.np;
+
+  Partial st[HPW];
+#pragma unroll
+  for (int k = 0; k < HPW; ++k) st[k] = Partial{kNegInf, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
+  for (int p0 = lg; p0 < np; p0 += LPW * U) {
+    f32x4 v[HPW][U];
+    float2 m[HPW][U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int pc = min(p0 + u * LPW, np - 1);          // always a written record
+      const long long rec = mg.rec0 + mg.step * pc + (pc == 0 ? mg.first : 0);
+#pragma unroll
+      for (int k = 0; k < HPW; ++k) {
+        const int h = min(wave + k * W, G - 1);
+        m[k][u] = load_dev(a.ws_ml + rec * G + h);
+        v[k][u] = load_dev(a.ws_acc + rec_acc_index(slice, rec, h, G, R) + 4 * q4);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < HPW; ++k) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool ok = p0 + u * LPW < np && m[k][u].x != kNegInf;
+        combine_into(st[k], ok ? m[k][u].x : kNegInf, ok ? m[k][u].y : 0.f,
+                     ok ? m[k][u].y * v[k][u] : f32x4{0.f, 0.f, 0.f, 0.f});
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < HPW; ++k) {
+    const int h = wave + k * W;
+    if (h >= G) break;
+#pragma unroll
+    for (int x = QL; x < 64; x <<= 1) {
+      const float om = __shfl_xor(st[k].m, x, 64);
+      const float ow = __shfl_xor(st[k].w, x, 64);
+      f32x4 oa;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) oa[e] = __shfl_xor(st[k].a[e], x, 64);
+      combine_into(st[k], om, ow, oa);
+    }
+    if (lane < QL) {
+      const f32x4 y = st[k].a * (1.f / st[k].w);
+      uint16_t* o = static_cast<uint16_t*>(a.out) +
+                    ((size_t)s * a.num_heads + unit * G + h) * D + 4 * ql;
+      const u32x2 packed = {DT::bits(y[0]) | (DT::bits(y[1]) << 16),
+                            DT::bits(y[2]) | (DT::bits(y[3]) << 16)};
+      *reinterpret_cast<u32x2*>(o) = packed;
+    }
+  }
+}
+
+// Fused combine: called by the whole workgroup right after wave 0 has written a
+// partial record of segment mg.seg with device-scope stores (wave 0 wrote every
+// word of it).  Wave 0 waits until those stores are acknowledged, i.e. visible
+// at device scope, then draws a ticket; the workgroup that draws np - 1 reads
+// the records back with device-scope loads, merges them and resets the
+// counter, so the ticket area is zero again when the kernel ends.
+template <int D, class DT, int W>
+__device__ __forceinline__ void finish_partial(const DecodeArgs& a, Phase1Lds<D, W>& sm, int s,
+                                               int unit, const SegMerge& mg) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    unsigned t = 0;
+    if (lane == 0)
+      t = __hip_atomic_fetch_add(a.tickets + mg.seg, 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+    t = __shfl(t, 0, 64);
+    if (lane == 0) sm.last = t == static_cast<unsigned>(mg.np - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(sm.last)) {
+    switch (a.group) {
+#define PA_MERGE_CASE(g) \
+      case g: merge_records<D, DT, g, W>(a, s, unit, mg); break;
+      PA_MERGE_CASE(1) PA_MERGE_CASE(2) PA_MERGE_CASE(3) PA_MERGE_CASE(4)
+      PA_MERGE_CASE(5) PA_MERGE_CASE(6) PA_MERGE_CASE(7) PA_MERGE_CASE(8)
+      PA_MERGE_CASE(9) PA_MERGE_CASE(10) PA_MERGE_CASE(11) PA_MERGE_CASE(12)
+      PA_MERGE_CASE(13) PA_MERGE_CASE(14) PA_MERGE_CASE(15) PA_MERGE_CASE(16)
+#undef PA_MERGE_CASE
+      default: break;
+    }
+    if (threadIdx.x == 0)
+      __hip_atomic_store(a.tickets + mg.seg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // Runs one piece with the whole workgroup.  `final` writes the output rows of
-// the group; otherwise the piece's partial goes to record `rec`.  Starts with a
-// barrier, so LDS from a previous piece may be reused.
+// the group; otherwise the piece's partial goes to record `rec`, and with the
+// fused combine the segment described by `mg` is merged by whichever workgroup
+// finishes its last partial.  Starts with a barrier, so LDS from a previous piece
+// may be reused.
 template <int D, class DT, int W>
 __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& sm, int s,
                                           int unit, int t_begin, int t_end, bool final,
-                                          long long rec) {
+                                          long long rec, const SegMerge& mg) {
   constexpr int KS = D / 32;               // k-steps of the QK^T MFMA (32 dims each)
   constexpr int DB = D / 16;               // 16-wide head_dim blocks of the PV MFMA
   constexpr int LOADS = D / 32;            // 16-byte loads per lane per tile (K or V)
@@ -437,6 +617,11 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& 
                                 DT::bits(y[2]) | (DT::bits(y[3]) << 16)};
           *reinterpret_cast<u32x2*>(o + 16 * c) = packed;
         }
+      } else if (a.tickets != nullptr) {
+#pragma unroll
+        for (int c = 0; c < DB; ++c)
+          store_dev(a.ws_acc + rec_acc_index(c, rec, col, G, a.records) + 4 * grp, acc[c] * inv);
+        if (grp == 0) store_dev(a.ws_ml + rec * G + col, make_float2(M, Lsum));
       } else {
 #pragma unroll
         for (int c = 0; c < DB; ++c)
@@ -446,6 +631,7 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& 
       }
     }
   }
+  if (!final && a.tickets != nullptr && mg.seg >= 0) finish_partial<D, DT, W>(a, sm, s, unit, mg);
 }
 
 // Grid mode: workgroup (partition, sequence, KV head), partition slowest.
@@ -470,8 +656,16 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_kernel(DecodeArgs a) 
     t_begin = part * a.partition_size;
     t_end = min(L, t_begin + a.partition_size);
   }
-  const long long rec = ((long long)s * a.units + unit) * a.max_parts + part;
-  run_piece<D, DT, W>(a, sm, s, unit, t_begin, t_end, single, rec);
+  const long long seg = (long long)s * a.units + unit;
+  const long long rec = seg * a.max_parts + part;
+  SegMerge mg{-1, 0, 0, 0, 0};
+  if (!single) {
+    mg.seg = static_cast<int>(seg);
+    mg.np = (L + a.partition_size - 1) / a.partition_size;
+    mg.rec0 = seg * a.max_parts;
+    mg.step = 1;
+  }
+  run_piece<D, DT, W>(a, sm, s, unit, t_begin, t_end, single, rec, mg);
 }
 
 // Balanced mode.  Sequence s has n(s) = ceil(L_s/16) tiles per KV head; laid end
@@ -543,19 +737,44 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(Decod
     }
   }
 
+  // share holding tile t: largest j with T*j/NS <= t
+  auto share_of = [&](long long t) { return ((t + 1) * NS - 1) / T; };
+  // the records of sequence s's partials: slot 1 of the share that begins it, then
+  // slot 0 of each following share up to the one holding its last tile
+  auto seg_merge = [&](int s) {
+    const long long j0 = share_of(uniform(pre[s]));
+    const long long j1 = share_of(uniform(pre[s + 1]) - 1);
+    return SegMerge{s * Hkv + kvh, static_cast<int>(j1 - j0 + 1), 2 * (j0 * Hkv + kvh),
+                    2LL * Hkv, 1};
+  };
+  // the sequence holding tile t < T: largest s with pre[s] <= t (it has tiles)
+  auto seq_of = [&](long long t) {
+    int s = 0, top = S - 1;
+    while (s < top) {
+      const int mid = (s + top + 1) >> 1;
+      if (uniform(pre[mid]) <= t) s = mid; else top = mid - 1;
+    }
+    return s;
+  };
+
   int job_q = -1, job_n = 0;
   if (lo == hi) {
     // an empty share (fewer tiles than shares) may lie inside a sequence that
     // neighbouring shares split: leave the identity (-inf, 0) in slot 0
-    for (int h = tid; h < a.group; h += NT)
-      a.ws_ml[2LL * w * a.group + h] = make_float2(kNegInf, 0.f);
-  } else {
-    // the sequence holding tile lo: largest s with pre[s] <= lo (it has tiles)
-    int s = 0, top = S - 1;
-    while (s < top) {
-      const int mid = (s + top + 1) >> 1;
-      if (uniform(pre[mid]) <= lo) s = mid; else top = mid - 1;
+    for (int h = tid; h < a.group; h += NT) {
+      if (a.tickets != nullptr)
+        store_dev(a.ws_ml + 2LL * w * a.group + h, make_float2(kNegInf, 0.f));
+      else
+        a.ws_ml[2LL * w * a.group + h] = make_float2(kNegInf, 0.f);
     }
+    if (a.tickets != nullptr && lo > 0 && lo < T) {
+      // inside sequence s iff tiles lo - 1 and lo both belong to it; the identity
+      // then counts among its partials
+      const int s = seq_of(lo);
+      if (uniform(pre[s]) < lo) finish_partial<D, DT, W>(a, sm, s, kvh, seg_merge(s));
+    }
+  } else {
+    int s = seq_of(lo);
     int x = static_cast<int>(lo);
     const int x_end = static_cast<int>(hi);
     while (x < x_end) {
@@ -573,7 +792,8 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(Decod
       }
       // the piece ends at its last tile, or at the sequence's last token
       const int t_end = tb == n ? kTile * (n - 1) + uniform(last_len[s]) : kTile * tb;
-      run_piece<D, DT, W>(a, sm, s, kvh, kTile * ta, t_end, final, rec);
+      run_piece<D, DT, W>(a, sm, s, kvh, kTile * ta, t_end, final, rec,
+                          final ? SegMerge{-1, 0, 0, 0, 0} : seg_merge(s));
       x = min(seg1, x_end);
       do { ++s; } while (s < S && uniform(pre[s + 1]) == uniform(pre[s]) && x < x_end);
     }
@@ -586,22 +806,6 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(Decod
 // ---------------------------------------------------------------------------
 constexpr int kRedThreads = 256;
 constexpr int kRedWaves = kRedThreads / 64;
-
-// Merge of two compound partials (m, w, a): m is a base-2 max, w the weight sum
-// and a the weighted sum, both relative to m.  (-inf, 0, 0) is the identity.
-struct Partial {
-  float m, w;
-  f32x4 a;
-};
-
-__device__ __forceinline__ void combine_into(Partial& x, float om, float ow, f32x4 oa) {
-  const float nm = fmaxf(x.m, om);
-  const float fx = nm == kNegInf ? 0.f : __builtin_amdgcn_exp2f(x.m - nm);
-  const float fo = nm == kNegInf ? 0.f : __builtin_amdgcn_exp2f(om - nm);
-  x.w = x.w * fx + ow * fo;
-  x.a = x.a * fx + oa * fo;
-  x.m = nm;
-}
 
 // Workgroup = (segment, SPW consecutive 16-wide head_dim slices).  Thread
 // (pg, ql) covers head_dim values 4*ql .. +3 of the workgroup's slices and folds
@@ -716,6 +920,12 @@ __global__ __launch_bounds__(kRedThreads) void pa_reduce_kernel(DecodeArgs a) {
                           DT::bits(y[2]) | (DT::bits(y[3]) << 16)};
     *reinterpret_cast<u32x2*>(o) = packed;
   }
+}
+
+// Clears n 16-byte words (the fused combine's ticket area).
+__global__ __launch_bounds__(256) void pa_zero_kernel(u32x4* p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = u32x4{0, 0, 0, 0};
 }
 
 // ---------------------------------------------------------------------------

@@ -44,8 +44,15 @@ struct Plan {
   int num_wg = 0;        // phase-1 workgroups, balanced mode
   long long records = 0; // partial records in the workspace
   long long grid1 = 0, grid2 = 0;
-  size_t ws_ml_off = 0, ws_jobs_off = 0, ws_bytes = 0;
+  bool fused = false;    // partials merged in phase 1 (ticket counters), no phase 2
+  size_t ws_acc_off = 0, ws_ml_off = 0, ws_jobs_off = 0, ws_bytes = 0;
 };
+
+// Ticket counters of the fused combine sit at the start of every workspace that
+// holds records, whatever the plan, so a workspace cleared once stays valid for
+// any later call: the other regions never overlap them.
+constexpr size_t kTicketBytes = PA_WORKSPACE_TICKET_BYTES;
+constexpr long long kMaxTickets = kTicketBytes / sizeof(unsigned);
 
 bool supported_head_dim(int d) { return d == 128 || d == 256; }
 
@@ -126,8 +133,12 @@ int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int 
   if (pl.grid1 > std::numeric_limits<int>::max() || pl.grid2 > std::numeric_limits<int>::max())
     return PA_ERR_SHAPE;
   if (pl.records > 0) {
+    const long long segments = static_cast<long long>(S) * pl.units;
+    pl.fused = opt && opt->fused_combine && segments <= kMaxTickets;
+    if (pl.fused) pl.grid2 = 0;
     const size_t recs = static_cast<size_t>(pl.records) * pl.group;   // (record, head) pairs
-    pl.ws_ml_off = align256(recs * D * sizeof(float));
+    pl.ws_acc_off = kTicketBytes;
+    pl.ws_ml_off = pl.ws_acc_off + align256(recs * D * sizeof(float));
     pl.ws_bytes = pl.ws_ml_off + recs * sizeof(float2);
     if (pl.balanced) {
       pl.ws_jobs_off = align256(pl.ws_bytes);
@@ -262,6 +273,7 @@ PA_API int paged_attn_plan(const int32_t* seq_lens_host, int num_seqs, int num_h
   info->threads_per_workgroup = kWaves * 64;
   info->lds_bytes_phase1 = kWaves * 2 * pa::kTile * head_dim * 2;
   info->balanced = pl.balanced ? 1 : 0;
+  info->fused = pl.fused ? 1 : 0;
   if (seq_lens_host) {
     if (pl.balanced) {
       // host mirror of the device split: sequence s covers tiles [pre_s, pre_s + n)
@@ -334,7 +346,8 @@ PA_API int paged_attn_decode_ex(void* out, const void* q, const void* key_cache,
   args.bt = block_tables;
   args.seq_lens = seq_lens;
   char* ws = static_cast<char*>(workspace);
-  args.ws_acc = pl.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  args.ws_acc = pl.ws_bytes ? reinterpret_cast<float*>(ws + pl.ws_acc_off) : nullptr;
+  args.tickets = pl.fused ? reinterpret_cast<unsigned*>(ws) : nullptr;
   args.ws_ml = pl.ws_bytes ? reinterpret_cast<float2*>(ws + pl.ws_ml_off) : nullptr;
   args.jobs = pl.balanced && pl.ws_bytes ? reinterpret_cast<int2*>(ws + pl.ws_jobs_off) : nullptr;
   args.records = pl.records;
@@ -371,6 +384,18 @@ PA_API int paged_attn_decode(void* out, const void* q, const void* key_cache,
                               num_heads, num_kv_heads, head_dim, block_size, scale,
                               partition_size, workspace, stream, max_blocks_per_seq,
                               max_seq_len, dtype, workspace_bytes, nullptr);
+}
+
+PA_API int paged_attn_workspace_init(void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  if (workspace_bytes == 0) return PA_OK;
+  if (!workspace) return PA_ERR_NULL;
+  if (!aligned(workspace, 256)) return PA_ERR_ALIGN;
+  const size_t n = (workspace_bytes < kTicketBytes ? workspace_bytes : kTicketBytes) / 16;
+  if (n == 0) return PA_OK;
+  hipLaunchKernelGGL(pa::pa_zero_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                     0, stream, static_cast<pa::u32x4*>(workspace), n);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 PA_API int paged_attn_gather_probe(void* k_out, void* v_out, const void* key_cache,

@@ -21,7 +21,10 @@
  *     87a19d2 online-softmax fix);
  *   - a length-tiered dispatch runs short sequences in one pass and splits long
  *     ones into partitions (b80fd2b, three-tier decode dispatch; 8d26e23, the
- *     partition size should be tunable).
+ *     partition size should be tunable);
+ *   - optionally, the merge runs inside phase 1 instead of a second kernel: the
+ *     cross-partition combine that is level 3 of the three-level decomposition
+ *     (8d26e23), the last workgroup of a sequence found by an atomic ticket.
  *
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers unless a parameter says "host".
@@ -65,6 +68,10 @@
 extern "C" {
 #endif
 
+/* Bytes at the start of every non-empty workspace reserved for the ticket
+ * counters of the fused combine (pa_options.fused_combine). */
+#define PA_WORKSPACE_TICKET_BYTES 65536
+
 typedef enum pa_dtype_t {
     PA_F16 = 0,
     PA_BF16 = 1
@@ -102,7 +109,17 @@ typedef struct pa_options {
      * KV head (the GQA-unaware grid; each KV page is read once per query head).
      * Uses fixed partitions (partition_size, or 0 for one workgroup per CU). */
     int per_query_head;
-    int reserved[3];
+    /* 1: merge the partials of each partitioned sequence inside phase 1 (the
+     * workgroup that finishes a sequence's last partial merges them, found by a
+     * device-scope atomic ticket) instead of launching phase 2.  The ticket
+     * counters occupy the first PA_WORKSPACE_TICKET_BYTES of the workspace: they
+     * must be zero before the first fused call on a workspace
+     * (paged_attn_workspace_init), and every fused call that completes leaves
+     * them zero.  Calls sharing a workspace must not overlap.  Ignored (phase 2
+     * runs) when num_seqs * num_kv_heads (num_heads with per_query_head)
+     * exceeds PA_WORKSPACE_TICKET_BYTES / 4. */
+    int fused_combine;
+    int reserved[2];
     /* If non-NULL, hipEventRecord(phase1_begin/phase1_end, stream) is issued
      * immediately before/after the phase-1 kernel (instrumentation only). */
     hipEvent_t phase1_begin;
@@ -124,6 +141,7 @@ typedef struct pa_plan_info {
     int threads_per_workgroup; /* phase-1 block size                        */
     int lds_bytes_phase1;      /* LDS of the phase-1 tile slots             */
     int balanced;              /* 1: length-balanced split (partition_size 0) */
+    int fused;                 /* 1: partials merged in phase 1, no phase-2 launch */
 } pa_plan_info;
 
 /*
@@ -132,9 +150,11 @@ typedef struct pa_plan_info {
  * table capacity max_blocks_per_seq*block_size is used.  Returns (size_t)-1 for
  * arguments paged_attn_decode would reject.
  *
- * The workspace holds, for each (sequence, query head, partition), the phase-1
- * partial: weighted_v as head_dim fp32 values, then (max_score, exp_sum) as two
- * fp32 values, with max_score in base-2 units (log2(e)*scale*q.k).
+ * The workspace starts with PA_WORKSPACE_TICKET_BYTES of ticket counters (used
+ * only by the fused combine, never touched otherwise), then holds, for each
+ * (sequence, query head, partition), the phase-1 partial: weighted_v as head_dim
+ * fp32 values, then (max_score, exp_sum) as two fp32 values, with max_score in
+ * base-2 units (log2(e)*scale*q.k).
  */
 size_t paged_attn_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                                  int block_size, int max_blocks_per_seq, int max_seq_len,
@@ -194,6 +214,16 @@ int paged_attn_decode_ex(void* out, const void* q, const void* key_cache,
                          int partition_size, void* workspace, hipStream_t stream,
                          int max_blocks_per_seq, int max_seq_len, int dtype,
                          size_t workspace_bytes, const pa_options* opt);
+
+/*
+ * Clears the ticket area (the first min(workspace_bytes,
+ * PA_WORKSPACE_TICKET_BYTES) bytes) of a workspace with a kernel on `stream`, as
+ * the fused combine (pa_options.fused_combine) needs before the first call on a
+ * new workspace, or after a call that failed.  workspace: device pointer,
+ * 256-byte aligned (NULL only with workspace_bytes 0).  Returns PA_OK,
+ * PA_ERR_NULL, PA_ERR_ALIGN or PA_ERR_HIP.
+ */
+int paged_attn_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Human-readable text for a pa_status_t (static storage, never NULL). */
 const char* paged_attn_status_str(int status);

@@ -89,13 +89,14 @@ def test_workspace_size_formula(lib):
     n = lib.paged_attn_workspace_size(S, Hq, Hkv, D, bs, mbps, 102400, P)
     parts = 102400 // P
     acc = S * Hq * parts * D * 4
-    assert n == ((acc + 255) // 256) * 256 + S * Hq * parts * 8
+    tickets = 65536                      # PA_WORKSPACE_TICKET_BYTES, first in every workspace
+    assert n == tickets + ((acc + 255) // 256) * 256 + S * Hq * parts * 8
     # explicit partitions: every sequence fits one partition -> one pass, no workspace
     assert lib.paged_attn_workspace_size(256, 24, 4, 256, 32, 512, 16384, 16384) == 0
     # balanced split (partition_size 0): two records per phase-1 workgroup + a job each
     nw = 512
     recs = 2 * nw * 6
-    acc = ((recs * 256 * 4 + 255) // 256) * 256
+    acc = tickets + ((recs * 256 * 4 + 255) // 256) * 256
     ml = ((acc + recs * 8 + 255) // 256) * 256
     assert lib.paged_attn_workspace_size(256, 24, 4, 256, 32, 512, 16384, 0) == ml + nw * 8
     assert lib.paged_attn_workspace_size(2, 24, 5, 256, 16, 64, 0, 512) == ctypes.c_size_t(-1).value
@@ -224,3 +225,33 @@ def test_product_path_has_no_oracle_or_fallback():
     src = open(os.path.join(ROOT, "gqa_aware_paged_amd", "__init__.py")).read()
     assert "oracle" not in src.replace("no fallback", "")
     assert "raise RuntimeError" in src
+
+
+def test_fused_combine_plan(lib):
+    """The fused combine drops the phase-2 launch and keeps the workspace layout;
+    it is declined when the ticket area cannot hold one counter per segment."""
+    L, P = 102400, 512
+    base = pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, P)
+    fused = pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, P, fused_combine=True)
+    assert base["fused"] == 0 and base["phase2_workgroups"] == 4 * 4 * 16
+    assert fused["fused"] == 1 and fused["phase2_workgroups"] == 0
+    assert fused["phase1_workgroups"] == base["phase1_workgroups"]
+    assert fused["workspace_bytes"] == base["workspace_bytes"]
+    bal = pa.plan([64] * 60 + [65536] * 4, 24, 4, 256, 16, 4096, 65536, 0, fused_combine=True)
+    assert bal["balanced"] == 1 and bal["fused"] == 1 and bal["phase2_workgroups"] == 0
+    # all sequences in one pass: nothing to merge, no workspace, nothing fused
+    short = pa.plan([100] * 8, 24, 4, 256, 16, 8, 128, 128, fused_combine=True)
+    assert short["workspace_bytes"] == 0 and short["fused"] == 0
+    # 16384 counters: 4096 sequences x 4 KV heads fit, 683 x 24 query heads do not
+    ok = pa.plan(None, 24, 4, 256, 16, 64, 1024, 256, num_seqs=4096, fused_combine=True)
+    no = pa.plan(None, 24, 4, 256, 16, 64, 1024, 256, num_seqs=683, fused_combine=True,
+                 per_query_head=True)
+    assert ok["fused"] == 1 and no["fused"] == 0 and no["phase2_workgroups"] > 0
+
+
+def test_workspace_init_validation(lib):
+    """Error paths only (a valid call launches a kernel)."""
+    stream = ctypes.c_void_p(0)
+    assert lib.paged_attn_workspace_init(None, 0, stream) == 0          # nothing to clear
+    assert lib.paged_attn_workspace_init(None, 4096, stream) == 1       # PA_ERR_NULL
+    assert lib.paged_attn_workspace_init(ctypes.c_void_p(0x10010), 4096, stream) == 7
