@@ -113,6 +113,10 @@ def main():
                     help="ablation: one workgroup per query head (KV read once per query head)")
     ap.add_argument("--fused", action="store_true",
                     help="merge partitions inside phase 1 (atomic ticket) instead of a phase-2 launch")
+    ap.add_argument("--head-dim", type=int, default=256,
+                    help="long workload only: head_dim for shape sweeps")
+    ap.add_argument("--block-size", type=int, default=16,
+                    help="long workload only: block_size for shape sweeps")
     ap.add_argument("--no-hint", action="store_true",
                     help="do not pass the host-side total of seq_lens to the planner")
     ap.add_argument("--num-cus", type=int, default=0,
@@ -141,7 +145,11 @@ def main():
     pa.lib()
 
     log(f"generating workload {args.workload}")
-    w = workloads.NAMED[args.workload](device="cuda")
+    if args.workload == "long":
+        w = workloads.long_context(device="cuda", head_dim=args.head_dim,
+                                   block_size=args.block_size)
+    else:
+        w = workloads.NAMED[args.workload](device="cuda")
     torch.cuda.synchronize()
 
     def decoder(P):

@@ -179,21 +179,43 @@ __device__ __forceinline__ int page_of(const int32_t* bt, int s, int t0, int bs,
   return __builtin_amdgcn_readfirstlane(bt[(size_t)s * mbps + blk]);
 }
 
-__device__ __forceinline__ size_t tile_offset(const int32_t* bt, int s, int t0, int kvh,
-                                              int Hkv, int bs, int mbps, int D) {
-  return tile_offset_in(page_of(bt, s, t0, bs, mbps), t0, kvh, Hkv, bs, D);
+// A tile is read as two 8-token halves.  Pages holding the halves of the tile
+// starting at t0 (wave-uniform): with block_size >= 16 both lie in one page; with
+// block_size 8 the second half has its own page, looked up only if it holds a
+// token before t_end (later block-table entries may be invalid), else the first
+// half is read again and masked like any slot past the end.
+__device__ __forceinline__ int2 tile_pages(const int32_t* bt, int s, int t0, int t_end, int bs,
+                                           int mbps) {
+  const int p0 = page_of(bt, s, t0, bs, mbps);
+  int p1 = p0;
+  if (bs < kTile && t0 + kTile / 2 < t_end) p1 = page_of(bt, s, t0 + kTile / 2, bs, mbps);
+  return make_int2(p0, p1);
 }
 
-// One 16-token tile is 16*D*2 bytes, contiguous.  Lane `lane` fetches the 16-byte
-// chunks lane, lane+64, ... so every load instruction covers 1 KiB contiguously.
-// K and V are read exactly once per step, so the loads are nontemporal: they do
-// not displace reusable lines from the caches (worth ~10% of gather bandwidth).
+// Element offsets of the two halves of the tile at t0 (see tile_pages); with one
+// page they are 8*D apart.
+__device__ __forceinline__ void tile_offsets(int2 pages, int t0, int kvh, int Hkv, int bs, int D,
+                                             size_t& lo, size_t& hi) {
+  lo = tile_offset_in(pages.x, t0, kvh, Hkv, bs, D);
+  hi = bs < kTile ? tile_offset_in(pages.y, t0 + kTile / 2, kvh, Hkv, bs, D) : lo + 8 * D;
+}
+
+// One 16-token tile is two 8-row halves of 8*D*2 bytes, each contiguous.  Lane
+// `lane` fetches the 16-byte chunks lane, lane+64, ... of each half, so every
+// load instruction covers 1 KiB contiguously.  K and V are read exactly once per
+// step, so the loads are nontemporal: they do not displace reusable lines from
+// the caches (worth ~10% of gather bandwidth).
 template <int D>
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ src, int lane,
+__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ lo,
+                                          const uint16_t* __restrict__ hi, int lane,
                                           u32x4 (&r)[D / 32]) {
-  const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
+  constexpr int H = D / 64;                // loads per half
+  const u32x4* a = reinterpret_cast<const u32x4*>(lo);
+  const u32x4* b = reinterpret_cast<const u32x4*>(hi);
 #pragma unroll
-  for (int j = 0; j < D / 32; ++j) r[j] = __builtin_nontemporal_load(s4 + j * 64 + lane);
+  for (int j = 0; j < H; ++j) r[j] = __builtin_nontemporal_load(a + j * 64 + lane);
+#pragma unroll
+  for (int j = 0; j < H; ++j) r[H + j] = __builtin_nontemporal_load(b + j * 64 + lane);
 }
 
 // LDS slot of one tile: 16 rows of D halves; 16-byte chunk c of row t is stored at
@@ -205,14 +227,17 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ src, int 
 //    4q..4q+3 per 16 lanes): f(t) = t ^ 8*(t & 1), conflict-free, where f(t) = t
 //    costs two extra cycles per read.
 // Staging writes (16 consecutive chunks of a row) are conflict-free either way.
+// With head_dim 64 a row has 8 chunks and the mask is cut to 3 bits.
 template <int D, bool kIsV = false>
 struct Swz {
   static constexpr int kChunks = D / 8;
-  static_assert(kChunks >= 16, "the swizzle spans 16 chunk columns");
+  static_assert(kChunks >= 8 && (kChunks & (kChunks - 1)) == 0, "8, 16 or 32 chunks per row");
   static __device__ __forceinline__ int f(int row) {
     return kIsV ? (row ^ ((row & 1) << 3)) : row;
   }
-  static __device__ __forceinline__ int chunk(int row, int c) { return c ^ f(row & 15); }
+  static __device__ __forceinline__ int chunk(int row, int c) {
+    return c ^ (f(row & 15) & (kChunks - 1));
+  }
   static __device__ __forceinline__ int byte_off(int row, int c) {
     return row * (D * 2) + chunk(row, c) * 16;
   }
@@ -465,13 +490,17 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& 
   const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
   const int bs = a.block_size, mbps = a.max_blocks_per_seq;
   int it = wave;
-  int page_cur = it < n_tiles ? page_of(a.bt, s, t_begin + kTile * it, bs, mbps) : 0;
-  int page_next = it + W < n_tiles ? page_of(a.bt, s, t_begin + kTile * (it + W), bs, mbps) : 0;
+  const int2 page_cur = it < n_tiles ? tile_pages(a.bt, s, t_begin + kTile * it, t_end, bs, mbps)
+                                     : make_int2(0, 0);
+  int2 page_next = it + W < n_tiles
+                       ? tile_pages(a.bt, s, t_begin + kTile * (it + W), t_end, bs, mbps)
+                       : make_int2(0, 0);
   u32x4 rk[LOADS], rv[LOADS];
   if (it < n_tiles) {
-    const size_t off = tile_offset_in(page_cur, t_begin + kTile * it, kvh, Hkv, bs, D);
-    load_tile<D>(a.kc + off, lane, rk);
-    load_tile<D>(a.vc + off, lane, rv);
+    size_t lo, hi;
+    tile_offsets(page_cur, t_begin + kTile * it, kvh, Hkv, bs, D, lo, hi);
+    load_tile<D>(a.kc + lo, a.kc + hi, lane, rk);
+    load_tile<D>(a.vc + lo, a.vc + hi, lane, rv);
   }
 
   // Q of the group in LDS as the B operand of S^T = K Q^T: row h is query head
@@ -509,10 +538,12 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& 
     // prefetch the wave's next tile while this one is consumed, and the page id of
     // the one after
     if (it + W < n_tiles) {
-      const size_t off = tile_offset_in(page_next, t0 + kTile * W, kvh, Hkv, bs, D);
-      load_tile<D>(a.kc + off, lane, rk);
-      load_tile<D>(a.vc + off, lane, rv);
-      if (it + 2 * W < n_tiles) page_next = page_of(a.bt, s, t0 + 2 * kTile * W, bs, mbps);
+      size_t lo, hi;
+      tile_offsets(page_next, t0 + kTile * W, kvh, Hkv, bs, D, lo, hi);
+      load_tile<D>(a.kc + lo, a.kc + hi, lane, rk);
+      load_tile<D>(a.vc + lo, a.vc + hi, lane, rv);
+      if (it + 2 * W < n_tiles)
+        page_next = tile_pages(a.bt, s, t0 + 2 * kTile * W, t_end, bs, mbps);
     }
 
     // S^T[token, head] = sum_d K[token, d] Q[head, d]
@@ -943,11 +974,12 @@ __global__ __launch_bounds__(256) void pa_gather_kernel(GatherArgs a) {
   const int n_tiles = L > 0 ? (L + kTile - 1) / kTile : 0;
   for (int it = wave; it < n_tiles; it += 4) {
     const int t0 = kTile * it;
-    const size_t off = tile_offset(a.bt, s, t0, kvh, a.num_kv_heads, a.block_size,
-                                   a.max_blocks_per_seq, D);
+    size_t lo, hi;
+    tile_offsets(tile_pages(a.bt, s, t0, L, a.block_size, a.max_blocks_per_seq), t0, kvh,
+                 a.num_kv_heads, a.block_size, D, lo, hi);
     u32x4 rk[LOADS], rv[LOADS];
-    load_tile<D>(a.kc + off, lane, rk);
-    load_tile<D>(a.vc + off, lane, rv);
+    load_tile<D>(a.kc + lo, a.kc + hi, lane, rk);
+    load_tile<D>(a.vc + lo, a.vc + hi, lane, rv);
     const size_t dst = (((size_t)s * a.num_kv_heads + kvh) * a.max_seq_len + t0) * D;
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {

@@ -33,6 +33,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMinTilesPerWG = 16;        // balanced mode: at least 4 tiles per wave
 constexpr int kBalancedSlices = 8;        // balanced phase 2: 16-wide slices per workgroup
 
+// 16-wide head_dim slices one balanced phase-2 workgroup merges
+constexpr int balanced_slices(int D) { return D / 16 < kBalancedSlices ? D / 16 : kBalancedSlices; }
+
 struct Plan {
   bool balanced = false; // length-balanced split (partition_size 0) vs fixed partitions
   int P = 0;             // partition size (tokens), grid mode
@@ -54,7 +57,7 @@ struct Plan {
 constexpr size_t kTicketBytes = PA_WORKSPACE_TICKET_BYTES;
 constexpr long long kMaxTickets = kTicketBytes / sizeof(unsigned);
 
-bool supported_head_dim(int d) { return d == 128 || d == 256; }
+bool supported_head_dim(int d) { return d == 64 || d == 128 || d == 256; }
 
 // Validation shared by every entry point (pointers excepted).
 int check_sizes(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int P, int dtype) {
@@ -64,7 +67,7 @@ int check_sizes(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, in
   if (dtype != PA_F16 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   if (!supported_head_dim(D)) return PA_ERR_UNSUPPORTED;
   if (Hq / Hkv > 16) return PA_ERR_UNSUPPORTED;
-  if (bs % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (bs != 8 && bs % 16 != 0) return PA_ERR_UNSUPPORTED;
   if (S > 0 && mbps < 1) return PA_ERR_SHAPE;
   const long long cap = static_cast<long long>(mbps) * bs;
   if (max_len > cap) return PA_ERR_SHAPE;
@@ -118,7 +121,7 @@ int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int 
     pl.num_wg = static_cast<int>(ns * Hkv);
     pl.records = 2LL * pl.num_wg;
     pl.grid1 = pl.num_wg;
-    pl.grid2 = static_cast<long long>(pl.num_wg) * (D / 16 / kBalancedSlices);
+    pl.grid2 = static_cast<long long>(pl.num_wg) * (D / 16 / balanced_slices(D));
     pl.T1 = -1;
   } else {
     pl.P = P_req > 0 ? P_req : auto_partition(S, pl.units, pl.max_seq_len, cus, hint);
@@ -155,7 +158,7 @@ template <int D, class DT, int G>
 void launch_reduce_g(bool balanced, unsigned grid, hipStream_t stream,
                      const pa::DecodeArgs& args) {
   if (balanced)
-    hipLaunchKernelGGL((pa::pa_reduce_kernel<D, DT, G, kBalancedSlices, true>), dim3(grid),
+    hipLaunchKernelGGL((pa::pa_reduce_kernel<D, DT, G, balanced_slices(D), true>), dim3(grid),
                        dim3(pa::kRedThreads), 0, stream, args);
   else
     hipLaunchKernelGGL((pa::pa_reduce_kernel<D, DT, G, 1, false>), dim3(grid),
@@ -219,8 +222,8 @@ PA_API const char* paged_attn_status_str(int status) {
     case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
     case PA_ERR_SHAPE: return "PA_ERR_SHAPE: inconsistent sizes";
     case PA_ERR_UNSUPPORTED:
-      return "PA_ERR_UNSUPPORTED: head_dim must be 128 or 256, group 1..16, block_size a "
-             "multiple of 16, dtype f16 or bf16";
+      return "PA_ERR_UNSUPPORTED: head_dim must be 64, 128 or 256, group 1..16, block_size 8 "
+             "or a multiple of 16, dtype f16 or bf16";
     case PA_ERR_PARTITION: return "PA_ERR_PARTITION: partition_size must be 0 or a multiple of 16";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: a HIP launch failed";
@@ -366,11 +369,15 @@ PA_API int paged_attn_decode_ex(void* out, const void* q, const void* key_cache,
   args.max_parts = pl.max_parts;
   args.scale_log2 = scale * kLog2e;
 
-  if (head_dim == 256)
-    return dtype == PA_F16 ? launch_decode<256, pa::F16>(args, pl, stream, opt)
-                           : launch_decode<256, pa::BF16>(args, pl, stream, opt);
-  return dtype == PA_F16 ? launch_decode<128, pa::F16>(args, pl, stream, opt)
+  const bool f16 = dtype == PA_F16;
+  switch (head_dim) {
+    case 256: return f16 ? launch_decode<256, pa::F16>(args, pl, stream, opt)
+                         : launch_decode<256, pa::BF16>(args, pl, stream, opt);
+    case 128: return f16 ? launch_decode<128, pa::F16>(args, pl, stream, opt)
                          : launch_decode<128, pa::BF16>(args, pl, stream, opt);
+    default: return f16 ? launch_decode<64, pa::F16>(args, pl, stream, opt)
+                        : launch_decode<64, pa::BF16>(args, pl, stream, opt);
+  }
 }
 
 PA_API int paged_attn_decode(void* out, const void* q, const void* key_cache,
@@ -419,11 +426,12 @@ PA_API int paged_attn_gather_probe(void* k_out, void* v_out, const void* key_cac
                    static_cast<const uint16_t*>(key_cache),
                    static_cast<const uint16_t*>(value_cache), block_tables, seq_lens,
                    num_seqs, num_kv_heads, block_size, max_blocks_per_seq, max_seq_len};
+  const dim3 blocks(static_cast<unsigned>(grid));
   if (head_dim == 256)
-    hipLaunchKernelGGL(pa::pa_gather_kernel<256>, dim3(static_cast<unsigned>(grid)), dim3(256),
-                       0, stream, g);
+    hipLaunchKernelGGL(pa::pa_gather_kernel<256>, blocks, dim3(256), 0, stream, g);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL(pa::pa_gather_kernel<128>, blocks, dim3(256), 0, stream, g);
   else
-    hipLaunchKernelGGL(pa::pa_gather_kernel<128>, dim3(static_cast<unsigned>(grid)), dim3(256),
-                       0, stream, g);
+    hipLaunchKernelGGL(pa::pa_gather_kernel<64>, blocks, dim3(256), 0, stream, g);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

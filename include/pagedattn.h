@@ -51,9 +51,9 @@
  *   never read; slots at or past seq_lens[s] in the last page are never used
  *   (they may hold NaN).
  *
- * Supported shapes: head_dim 128 or 256; num_heads / num_kv_heads (the group)
- * 1..16; block_size a multiple of 16; partition_size 0 (automatic) or a positive
- * multiple of 16; dtype f16 or bf16 (q, caches and out share it).
+ * Supported shapes: head_dim 64, 128 or 256; num_heads / num_kv_heads (the
+ * group) 1..16; block_size 8 or a multiple of 16; partition_size 0 (automatic)
+ * or a positive multiple of 16; dtype f16 or bf16 (q, caches and out share it).
  * Pointers q, key_cache and value_cache must be 16-byte aligned, out 8-byte
  * aligned and workspace 256-byte aligned (every torch allocation is).
  */

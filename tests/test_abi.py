@@ -70,7 +70,9 @@ def test_validation_errors_before_any_launch(lib):
     assert call(lib, Hkv=5) == 2                     # 24 % 5 -> PA_ERR_SHAPE
     assert call(lib, D=96) == 3                      # PA_ERR_UNSUPPORTED
     assert call(lib, Hq=68, Hkv=4) == 3              # group 17 > 16
-    assert call(lib, bs=8) == 3                      # block size not a multiple of 16
+    assert call(lib, bs=24) == 3                     # block size neither 8 nor a multiple of 16
+    assert call(lib, bs=8, mbps=128) == 5            # 8 is supported (then: workspace missing)
+    assert call(lib, D=64) == 5                      # head_dim 64 is supported
     assert call(lib, dtype=2) == 3
     assert call(lib, P=24) == 4                      # PA_ERR_PARTITION
     assert call(lib, P=-16) == 4
@@ -217,7 +219,7 @@ def test_plan_rejects_what_decode_rejects(lib):
     with pytest.raises(pa.PagedAttnError, match="PARTITION"):
         pa.plan([10], 24, 4, 256, 16, 4, 0, 40)
     with pytest.raises(pa.PagedAttnError, match="UNSUPPORTED"):
-        pa.plan([10], 24, 4, 64, 16, 4, 0, 512)
+        pa.plan([10], 24, 4, 96, 16, 4, 0, 512)
 
 
 def test_product_path_has_no_oracle_or_fallback():

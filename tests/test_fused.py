@@ -107,7 +107,7 @@ def test_single_record_segments():
     assert_close(gpu_out(fused(w, 512, tier=0)), oracle_full(w), "fused/np=1")
 
 
-@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("heads", [(8, 8), (16, 8), (32, 4), (64, 4), (16, 1)])
 @pytest.mark.parametrize("P", [64, 0])
 def test_head_shapes(D, heads, P):

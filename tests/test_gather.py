@@ -30,7 +30,7 @@ def check(w, what):
     say(f"  {what}: gather bit-exact ({kb.size} elements each)")
 
 
-@pytest.mark.parametrize("bs", [16, 32, 64])
+@pytest.mark.parametrize("bs", [8, 16, 32, 64])
 def test_gather_bit_exact(bs):
     say(f"case gather bs={bs}")
     w = workloads.make_workload("g", [0, 1, 15, 16, 17, 100, 1000, 3001], block_size=bs,
@@ -49,3 +49,11 @@ def test_gather_head_dim_128_shared_pages():
     w = workloads.make_workload("g", [64, 200, 333], head_dim=128, num_heads=16, num_kv_heads=8,
                                 device="cuda", poison=True, seed=22, shared_prefix_blocks=3)
     check(w, "D128-shared")
+
+
+@pytest.mark.parametrize("bs", [8, 16])
+def test_gather_head_dim_64(bs):
+    say(f"case gather D=64 bs={bs}")
+    w = workloads.make_workload("g", [1, 8, 9, 24, 250, 1001], head_dim=64, num_heads=8,
+                                num_kv_heads=2, block_size=bs, device="cuda", poison=True, seed=23)
+    check(w, f"D64-bs{bs}")

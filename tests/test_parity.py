@@ -137,7 +137,7 @@ def test_balanced_falls_back_above_sequence_cap():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("bs", [8, 16, 32])
 @pytest.mark.parametrize("P", [16, 32, 256, 1024])
 def test_partition_sizes(dtype, bs, P):
     if P % bs and P < bs:
@@ -147,7 +147,7 @@ def test_partition_sizes(dtype, bs, P):
     assert_close(gpu_out(run(w, 0)), oracle_full(w), f"{dtype}/bs{bs}/P{P}")
 
 
-@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("heads", [(8, 8), (16, 8), (16, 4), (32, 4), (64, 4), (16, 1)])
 @pytest.mark.parametrize("tier", ["single", "partitioned", "balanced"])
 def test_head_shapes(D, heads, tier):
@@ -159,13 +159,15 @@ def test_head_shapes(D, heads, tier):
     assert_close(gpu_out(out), oracle_full(w), f"Hq{Hq}/Hkv{Hkv}/D{D}/{tier}")
 
 
+@pytest.mark.parametrize("bs", [8, 16])
 @pytest.mark.parametrize("tier", ["single", "partitioned", "balanced"])
-def test_edge_lengths(tier):
-    lens = [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1023, 1024, 1025, 0, 2]
-    say(f"case edge lengths tier={tier}")
-    w = make(lens, partition_size=512)
+def test_edge_lengths(tier, bs):
+    lens = [0, 1, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1023, 1024, 1025,
+            0, 2]
+    say(f"case edge lengths tier={tier} bs={bs}")
+    w = make(lens, partition_size=512, block_size=bs)
     out = gpu_out(run(w, P=0) if tier == "balanced" else run(w, TIERS[tier]))
-    assert np.all(out[0] == 0) and np.all(out[17] == 0)
+    assert np.all(out[0] == 0) and np.all(out[20] == 0)
     assert_close(out, oracle_full(w), f"edges/{tier}")
 
 

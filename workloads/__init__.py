@@ -249,12 +249,17 @@ def batch(device="cpu", poison=False, seed=1002):
                          poison=poison)
 
 
-def long_context(device="cpu", poison=False, seed=1003, num_seqs=4, seq_len=102400):
+def long_context(device="cpu", poison=False, seed=1003, num_seqs=4, seq_len=102400,
+                 head_dim=256, block_size=16):
     """4 seqs x 102400 tokens (200 partitions of 512), 24/4 heads, head_dim 256,
-    16-token pages, f16; K, V ~ N(0,1); q = 8 N(0,1) so the softmax is peaked."""
-    return make_workload(f"long-{num_seqs}x{seq_len}", [seq_len] * num_seqs,
-                         scale=1.0 / 16, partition_size=512, dtype="f16", q_mult=8.0,
-                         seed=seed, device=device, poison=poison)
+    16-token pages, f16; K, V ~ N(0,1); q = 8 N(0,1) so the softmax is peaked.
+    head_dim and block_size may be changed for shape sweeps (scale 1/sqrt(head_dim))."""
+    name = f"long-{num_seqs}x{seq_len}"
+    if head_dim != 256 or block_size != 16:
+        name += f"-D{head_dim}-bs{block_size}"
+    return make_workload(name, [seq_len] * num_seqs, head_dim=head_dim, block_size=block_size,
+                         scale=1.0 / math.sqrt(head_dim), partition_size=512, dtype="f16",
+                         q_mult=8.0, seed=seed, device=device, poison=poison)
 
 
 def mixed_lens(seed=1004, n=64):
