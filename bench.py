@@ -80,6 +80,15 @@ def traffic_from_counters(units_bytes):
     return fetch + write
 
 
+def default_command(args) -> bool:
+    """True when the run is the configuration the committed counters were taken on
+    (the long workload with automatic partitions and the host-side length total)."""
+    return (args.workload == "long" and args.partition_size == 0 and not args.p512
+            and args.single_pass_max_len is None and not args.per_query_head
+            and not args.fused and not args.no_hint and args.num_cus == 0
+            and args.head_dim == 256 and args.block_size == 16)
+
+
 def cpu_baseline(w, nseqs: int):
     """Time the fp64 oracle (as it stands) on the first `nseqs` sequences, all heads."""
     import oracle
@@ -272,7 +281,8 @@ def main():
                      "kernel": "pa_phase1_balanced_kernel" if info["balanced"] else "pa_phase1_kernel",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_counters(kv) if args.workload == "long" else None,
+                     # the committed counters cover the default command only
+                     "traffic": traffic_from_counters(kv) if default_command(args) else None,
                      "algorithmic_bytes_per_launch": kv, "bytes_per_unit": bytes_per_unit,
                      "units_per_launch": units,
                      "avg_launch_us": round(ph1_avg * 1e3, 2)},

@@ -75,14 +75,22 @@ int check_sizes(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, in
   return PA_OK;
 }
 
+// Resident phase-1 workgroups per CU the fixed partitions aim at.  Measured on
+// 4 x 102400 tokens: with head_dim 256 and pages of 16 or more tokens one
+// workgroup per CU streams fastest (6.5 TB/s; two: -3%); with head_dim 128 or 64,
+// or 8-token pages, a tile carries fewer bytes per page or per softmax step and a
+// second resident workgroup hides the per-tile latency (head_dim 64: 3.2 -> 5.4
+// TB/s; 128: 4.7 -> 6.1; 8-token pages: 5.0 -> 5.9).
+int workgroups_per_cu(int D, int bs) { return D >= 256 && bs >= 16 ? 1 : 2; }
+
 // Fixed partition size when the caller passes 0 but the balanced split does not
-// apply (a forced tier, or more sequences than it keeps in LDS): spread the
-// step's K/V over one workgroup per compute unit.  The work estimate is
-// num_seqs * max_seq_len tokens per KV head (exact for equal lengths), or the
-// caller's total-token hint.
-int auto_partition(long long S, int Hkv, int max_len, int cus, long long total_hint) {
+// apply (equal lengths declared, a forced tier, or more sequences than it keeps
+// in LDS): spread the step's K/V over `slots` workgroups (CUs times
+// workgroups_per_cu).  The work estimate is num_seqs * max_seq_len tokens per KV
+// head (exact for equal lengths), or the caller's total-token hint.
+int auto_partition(long long S, int Hkv, int max_len, long long slots, long long total_hint) {
   const long long tokens = total_hint > 0 ? total_hint : S * max_len;
-  long long p = (tokens * Hkv + cus - 1) / cus;
+  long long p = (tokens * Hkv + slots - 1) / slots;
   p = (p + 15) / 16 * 16;
   if (p < kMinAutoPartition) p = kMinAutoPartition;
   if (p > max_len) p = (max_len + 15) / 16 * 16;
@@ -124,7 +132,10 @@ int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int 
     pl.grid2 = static_cast<long long>(pl.num_wg) * (D / 16 / balanced_slices(D));
     pl.T1 = -1;
   } else {
-    pl.P = P_req > 0 ? P_req : auto_partition(S, pl.units, pl.max_seq_len, cus, hint);
+    pl.P = P_req > 0 ? P_req
+                     : auto_partition(S, pl.units, pl.max_seq_len,
+                                      static_cast<long long>(cus) * workgroups_per_cu(D, bs),
+                                      hint);
     // a sequence that fits in one partition is served in one pass
     pl.T1 = forced_tier ? opt->single_pass_max_len : pl.P;
     if (pl.max_seq_len > pl.T1) pl.max_parts = (pl.max_seq_len + pl.P - 1) / pl.P;

@@ -199,6 +199,10 @@ def test_automatic_partition_size_for_256_cus(lib):
     per_cu = -(-sum(lens) * 4 // 256)
     assert a["partition_size"] == 65536
     assert b["partition_size"] == -(-per_cu // 16) * 16 and b["partitioned_seqs"] == 4
+    # head_dim 128 / 64 and 8-token pages aim at two resident workgroups per CU
+    for D, bs in ((128, 16), (64, 16), (256, 8)):
+        info = pa.plan([L] * 4, 24, 4, D, bs, L // bs, L, 0, total_tokens_hint=4 * L)
+        assert info["partition_size"] == 3200 and info["phase1_workgroups"] == 512
 
 
 def test_tile_budget_against_pages(lib):
