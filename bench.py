@@ -231,6 +231,20 @@ def main():
     log(f"timed {args.steps} steps: {step_ms * 1e3:.1f} us/step (wall {wall:.3f} s); with "
         f"phase-1 events {step_ms_ev * 1e3:.1f} us/step, phase-1 avg {ph1_avg * 1e3:.1f} us, "
         f"median {ph1[len(ph1) // 2] * 1e3:.1f} us")
+    # timed region 3 (cold): each step alone, after a 1 GiB device write that evicts
+    # the step's K/V from L2 and the 256 MB Infinity Cache; median over the steps
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(min(args.steps, 50)):
+        flush.fill_(i & 255)
+        start.record(stream)
+        step(dec)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        cold.append(start.elapsed_time(stop))
+    del flush
+    cold_ms = sorted(cold)[len(cold) // 2]
+    log(f"cold: median {cold_ms * 1e3:.1f} us/step over {len(cold)} steps")
     # context: the pages' fixed 512-token partitions on the same inputs
     p512_ms = None
     if P != 512 and args.p512:
@@ -246,7 +260,11 @@ def main():
     bytes_per_unit = 2 * w.head_dim * 2
     kv = units * bytes_per_unit
     assert kv == w.kv_bytes
-    eff = kv / (step_ms * 1e-3) / 1e9
+    # the tiny and batch workloads' K/V fits (or nearly fits) in the caches, so their
+    # headline is the cold step; the larger ones stream from HBM either way (hot)
+    timing = "cold" if args.workload in ("tiny", "batch") else "hot"
+    head_ms = cold_ms if timing == "cold" else step_ms
+    eff = kv / (head_ms * 1e-3) / 1e9
     achieved = kv / (ph1_avg * 1e-3) / 1e9
     rec = {
         "metric": "decode attention us/step + effective KV-cache GB/s (% of HBM peak), 1 GPU",
@@ -255,8 +273,11 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 5),
-        "us_per_step": round(step_ms * 1e3, 2),
+        "ms_per_step": round(head_ms, 5),
+        "us_per_step": round(head_ms * 1e3, 2),
+        "timing": timing,
+        "us_per_step_hot": round(step_ms * 1e3, 2),
+        "us_per_step_cold": round(cold_ms * 1e3, 2),
         "pct_hbm_peak": round(100 * eff / HBM_PEAK_GBS, 2),
         "us_per_step_partition_512": None if p512_ms is None else round(p512_ms * 1e3, 2),
         "higher_is_better": True,

@@ -10,6 +10,10 @@ decode / decode_rows / gather / partials
     ctypes wrappers over pa_oracle.c, the plain fp64 definition of decode
     attention with the block-table gather (see that file's header for the
     citations).
+prefill
+    The plain fp64 definition of prefill over a paged context (pa_oracle.c,
+    orc_prefill): each new token attends to the cached context and, causally,
+    to the new tokens up to itself.
 combine / fold_partials / merge_once
     The partition merge.  The page of commit 8d26e23 (docs) defines the
     compound partial (max_score, exp_sum, weighted_v) and a combine that
@@ -65,7 +69,10 @@ def _lib():
         lib.orc_gather.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I]
         lib.orc_partials.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, D, I, I, I]
         lib.orc_convert.argtypes = [P, P, ctypes.c_int64, I]
-        for f in (lib.orc_decode, lib.orc_decode_rows, lib.orc_gather, lib.orc_partials):
+        lib.orc_prefill.argtypes = [P, P, I, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, D, I,
+                                    I]
+        for f in (lib.orc_decode, lib.orc_decode_rows, lib.orc_gather, lib.orc_partials,
+                  lib.orc_prefill):
             f.restype = I
         lib.orc_convert.restype = None
         _lib_handle = lib
@@ -141,6 +148,33 @@ def decode_rows(rows: Sequence, q, key_cache, value_cache, block_tables, seq_len
     _check(_lib().orc_decode_rows(_p(out), _p(r), r.shape[0], _p(qb), _p(kb), _p(vb), _p(bt),
                                   _p(sl), S, Hq, Hkv, D, bs, NB, bt.shape[1], float(scale),
                                   DTYPE_CODE[dtype], int(threads)))
+    return out
+
+
+def prefill(q, k_new, v_new, key_cache, value_cache, block_tables, ctx_lens, query_start,
+            scale: float, dtype: str, rows: Optional[Sequence] = None,
+            threads: int = 0) -> np.ndarray:
+    """fp64 prefill: q, k_new, v_new hold the new tokens of every sequence packed
+    ([T, Hq, D] and [T, Hkv, D]; sequence s owns rows query_start[s] ..
+    query_start[s+1]-1); ctx_lens[s] context tokens are in the paged caches.
+    Returns [T, Hq, D], or [len(rows), D] for the (row, query head) pairs in rows."""
+    qb, knb, vnb = bits(q), bits(k_new), bits(v_new)
+    kb, vb = bits(key_cache), bits(value_cache)
+    bt, cl, qs = _i32(block_tables), _i32(ctx_lens), _i32(query_start)
+    T, Hq, D = qb.shape
+    NB, Hkv, bs, D2 = kb.shape
+    S = cl.shape[0]
+    assert D2 == D and knb.shape == (T, Hkv, D) and vnb.shape == knb.shape
+    assert qs.shape == (S + 1,) and int(qs[-1]) == T
+    MB = bt.shape[1] if bt.ndim == 2 else 0
+    if rows is None:
+        r, n, out = None, 0, np.empty((T, Hq, D), np.float64)
+    else:
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 2))
+        n, out = r.shape[0], np.empty((r.shape[0], D), np.float64)
+    _check(_lib().orc_prefill(_p(out), None if r is None else _p(r), n, _p(qb), _p(knb),
+                              _p(vnb), _p(kb), _p(vb), _p(bt), _p(cl), _p(qs), S, Hq, Hkv, D,
+                              bs, NB, MB, float(scale), DTYPE_CODE[dtype], int(threads)))
     return out
 
 

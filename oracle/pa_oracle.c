@@ -1,5 +1,6 @@
 /*
- * CPU oracle for paged-attention decode.  TEST INFRASTRUCTURE ONLY: the tests,
+ * CPU oracle for paged-attention decode (and prefill over a paged context, see
+ * orc_prefill at the end).  TEST INFRASTRUCTURE ONLY: the tests,
  * the smoke check and the CPU-baseline leg of the benchmark call it; the
  * product path never does.  It shares no code, header or constant with the
  * GPU library.
@@ -299,4 +300,118 @@ int orc_partials(double* m_out, double* l_out, double* acc_out, const uint16_t* 
         }
     }
     return 0;
+}
+
+/*
+ * Prefill over a paged context: the prefix path of the page of commit b80fd2b
+ * (paged_attn.py: _forward_prefix_pytorch runs one online softmax over the
+ * context gathered from the caches by block id, then over the current chunk's
+ * own keys under the causal mask; rewrite item 1 gathers the context once).
+ * By definition, for sequence s with C = ctx_lens[s] cached tokens and new
+ * tokens n = 0 .. Qn-1 (Qn = qstart[s+1] - qstart[s]) held at rows
+ * r = qstart[s] + n of q, k_new and v_new, query head h attends to the context
+ * tokens t < C (in the caches through block_tables, as in decode) and to the new
+ * tokens j <= n:
+ *
+ *     out[r,h,:] = sum_u softmax_u( scale * q[r,h,:] . K_u ) * V_u
+ *
+ * evaluated in double precision with the keys in the order context, then new.
+ * C <= 0 means no context.
+ *
+ * Layouts: q, out [T][Hq][D]; k_new, v_new [T][Hkv][D]; qstart [S+1] with
+ * qstart[0] = 0 and T = qstart[S]; caches and tables as above.
+ * rows: NULL for every (row, head), else n_rows pairs (row, query head) and out
+ * is [n_rows][D].
+ */
+static int orc_prefill_row(double* out, const uint16_t* q, const uint16_t* kn,
+                           const uint16_t* vn, const uint16_t* kc, const uint16_t* vc,
+                           const int32_t* bt, int C, int r0, int n, int s, int h, int Hq,
+                           int Hkv, int D, int bs, int NB, int MB, double scale, int dtype,
+                           double* x) {
+    int g = Hq / Hkv;
+    int kvh = h / g;
+    int err = 0;
+    int r = r0 + n;
+    if (C < 0) C = 0;
+    const uint16_t* qrow = q + ((int64_t)r * Hq + h) * D;
+    int L = C + n + 1;
+    double m = -INFINITY;
+    for (int u = 0; u < L; ++u) {
+        const uint16_t* k = u < C ? orc_token(kc, bt, s, u, kvh, Hkv, bs, D, NB, MB, &err)
+                                  : kn + ((int64_t)(r0 + u - C) * Hkv + kvh) * D;
+        if (!k) return err;
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d) acc += orc_val(qrow[d], dtype) * orc_val(k[d], dtype);
+        x[u] = scale * acc;
+        if (x[u] > m) m = x[u];
+    }
+    for (int d = 0; d < D; ++d) out[d] = 0.0;
+    double Z = 0.0;
+    for (int u = 0; u < L; ++u) {
+        double w = exp(x[u] - m);
+        Z += w;
+        const uint16_t* v = u < C ? orc_token(vc, bt, s, u, kvh, Hkv, bs, D, NB, MB, &err)
+                                  : vn + ((int64_t)(r0 + u - C) * Hkv + kvh) * D;
+        if (!v) return err;
+        for (int d = 0; d < D; ++d) out[d] += w * orc_val(v[d], dtype);
+    }
+    for (int d = 0; d < D; ++d) out[d] /= Z;
+    return 0;
+}
+
+int orc_prefill(double* out, const int32_t* rows, int n_rows, const uint16_t* q,
+                const uint16_t* kn, const uint16_t* vn, const uint16_t* kc, const uint16_t* vc,
+                const int32_t* bt, const int32_t* ctx_lens, const int32_t* qstart, int S,
+                int Hq, int Hkv, int D, int bs, int NB, int MB, double scale, int dtype,
+                int nthreads) {
+    if (S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || NB < 0 || MB < 0) return -1;
+    if (Hq % Hkv) return -1;
+    if (qstart[0] != 0) return -1;
+    int64_t maxL = 1;
+    for (int s = 0; s < S; ++s) {
+        if (qstart[s + 1] < qstart[s]) return -1;
+        if (ctx_lens[s] > (int64_t)MB * bs) return -3;
+        int64_t L = (ctx_lens[s] > 0 ? ctx_lens[s] : 0) + (qstart[s + 1] - qstart[s]);
+        if (L > maxL) maxL = L;
+    }
+    int T = qstart[S];
+    /* sequence of every row */
+    int* seq = (int*)malloc(sizeof(int) * (T > 0 ? T : 1));
+    if (!seq) return -4;
+    for (int s = 0; s < S; ++s)
+        for (int r = qstart[s]; r < qstart[s + 1]; ++r) seq[r] = s;
+    int64_t total = rows ? n_rows : (int64_t)T * Hq;
+    int status = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+#pragma omp parallel
+    {
+        double* x = (double*)malloc(sizeof(double) * maxL);
+        if (!x) {
+#pragma omp atomic write
+            status = -4;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < total; ++i) {
+            if (!x) continue;
+            int r = rows ? rows[2 * i] : (int)(i / Hq);
+            int h = rows ? rows[2 * i + 1] : (int)(i % Hq);
+            int e;
+            if (r < 0 || r >= T || h < 0 || h >= Hq) {
+                e = -1;
+            } else {
+                int s = seq[r];
+                e = orc_prefill_row(out + i * D, q, kn, vn, kc, vc, bt, ctx_lens[s], qstart[s],
+                                    r - qstart[s], s, h, Hq, Hkv, D, bs, NB, MB, scale, dtype, x);
+            }
+            if (e) {
+#pragma omp atomic write
+                status = e;
+            }
+        }
+        free(x);
+    }
+    free(seq);
+    return status;
 }

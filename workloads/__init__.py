@@ -287,5 +287,69 @@ def saturation(device="cpu", poison=False, seed=1005, num_seqs=256, seq_len=1638
                          outlier_mult=20.0, seed=seed, device=device, poison=poison)
 
 
+@dataclasses.dataclass
+class PrefillWorkload:
+    """Prefill over a paged context: `ctx` holds the caches, block tables and
+    context lengths (its seq_lens); the new tokens of every sequence are packed
+    in q [T, Hq, D], k_new and v_new [T, Hkv, D], sequence s owning rows
+    query_start[s] .. query_start[s+1]-1."""
+    name: str
+    ctx: Workload
+    q: torch.Tensor
+    k_new: torch.Tensor
+    v_new: torch.Tensor
+    query_start: torch.Tensor
+    query_start_host: np.ndarray
+    q_lens_host: np.ndarray
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.query_start_host[-1])
+
+    @property
+    def max_q_len(self) -> int:
+        return int(self.q_lens_host.max()) if len(self.q_lens_host) else 0
+
+
+def make_prefill(name: str, ctx_lens: Sequence[int], q_lens: Sequence[int],
+                 num_heads: int = 24, num_kv_heads: int = 4, head_dim: int = 256,
+                 block_size: int = 16, dtype: str = "f16", scale: Optional[float] = None,
+                 seed: int = 0, device: str = "cpu", poison: bool = False,
+                 pool_factor: float = 1.5) -> PrefillWorkload:
+    """Seeded prefill workload: the context part is make_workload(ctx_lens) (a
+    context length of 0 gives a sequence with no cached tokens); the new tokens'
+    q, k and v are N(0,1) rounded to the dtype."""
+    ctx = make_workload(name, ctx_lens, num_heads=num_heads, num_kv_heads=num_kv_heads,
+                        head_dim=head_dim, block_size=block_size, dtype=dtype, scale=scale,
+                        seed=seed, device=device, poison=poison, pool_factor=pool_factor)
+    ql = np.asarray(q_lens, dtype=np.int64)
+    assert len(ql) == len(ctx_lens) and (ql >= 0).all()
+    qs = np.zeros(len(ql) + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(ql)
+    T = int(qs[-1])
+    tdt = DTYPES[dtype]
+    if device == "cpu":
+        gen = np.random.Generator(np.random.PCG64(seed + 500))
+    else:
+        gen = torch.Generator(device=device)
+        gen.manual_seed(seed + 1500)
+    q = _normal(gen, (T, num_heads, head_dim), device).to(tdt)
+    kn = _normal(gen, (T, num_kv_heads, head_dim), device).to(tdt)
+    vn = _normal(gen, (T, num_kv_heads, head_dim), device).to(tdt)
+    return PrefillWorkload(name=name, ctx=ctx, q=q, k_new=kn, v_new=vn,
+                           query_start=torch.from_numpy(qs).to(device), query_start_host=qs,
+                           q_lens_host=ql)
+
+
+def prefill_chunk(device="cpu", poison=False, seed=1006, num_seqs=4, ctx_len=16384,
+                  q_len=2048):
+    """Chunked prefill: 4 sequences with 16384 cached context tokens each and a
+    2048-token new chunk, 24/4 heads, head_dim 256, 16-token pages, f16 N(0,1),
+    scale 1/16."""
+    return make_prefill(f"prefill-{num_seqs}x({ctx_len}+{q_len})", [ctx_len] * num_seqs,
+                        [q_len] * num_seqs, scale=1.0 / 16, seed=seed, device=device,
+                        poison=poison)
+
+
 NAMED = {"tiny": tiny, "batch": batch, "long": long_context, "mixed": mixed,
          "saturation": saturation}
