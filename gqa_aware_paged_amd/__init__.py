@@ -20,7 +20,7 @@ PA_F16, PA_BF16 = 0, 1
 _DTYPE = {torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 SYMBOLS = ("paged_attn_workspace_size", "paged_attn_workspace_size_ex", "paged_attn_decode",
            "paged_attn_decode_ex", "paged_attn_status_str", "paged_attn_plan",
-           "paged_attn_gather_probe", "paged_attn_workspace_init")
+           "paged_attn_gather_probe", "paged_attn_workspace_init", "paged_attn_prefill")
 
 
 class Options(ctypes.Structure):
@@ -74,6 +74,9 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_gather_probe.restype = I
         L.paged_attn_workspace_init.argtypes = [P, Z, P]
         L.paged_attn_workspace_init.restype = I
+        L.paged_attn_prefill.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, I,
+                                         I, P]
+        L.paged_attn_prefill.restype = I
         _lib = L
     return _lib
 
@@ -248,6 +251,37 @@ def decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
         ctypes.c_void_p(stream), mbps, int(max_seq_len), _DTYPE[q.dtype],
         0 if workspace is None else workspace.numel() * workspace.element_size(),
         ctypes.byref(o)))
+    return out
+
+
+def prefill(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+            key_cache: torch.Tensor, value_cache: torch.Tensor, block_tables: torch.Tensor,
+            ctx_lens: torch.Tensor, query_start: torch.Tensor, scale: float,
+            max_query_len: int, max_ctx_len: int, out: Optional[torch.Tensor] = None,
+            stream: Optional[int] = None) -> torch.Tensor:
+    """Prefill over a paged context: new token n of sequence s (row query_start[s] + n
+    of q, k_new, v_new) attends to the ctx_lens[s] cached tokens and causally to
+    the new tokens up to itself.  max_query_len / max_ctx_len are host-side bounds."""
+    _validate(q, key_cache, value_cache, block_tables, ctx_lens)
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("query_start", query_start)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if k_new.dtype != q.dtype or v_new.dtype != q.dtype or query_start.dtype != torch.int32:
+        raise ValueError("k_new/v_new share q's dtype; query_start is int32")
+    T, Hq, D = q.shape
+    _, Hkv, bs, _ = key_cache.shape
+    S = ctx_lens.shape[0]
+    if k_new.shape != (T, Hkv, D) or v_new.shape != k_new.shape or query_start.shape != (S + 1,):
+        raise ValueError("k_new/v_new [T, Hkv, D]; query_start [S+1]")
+    if out is None:
+        out = torch.empty_like(q)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib().paged_attn_prefill(
+        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(key_cache), _ptr(value_cache),
+        _ptr(block_tables), _ptr(ctx_lens), _ptr(query_start), S, Hq, Hkv, D, bs, float(scale),
+        block_tables.shape[1], int(max_query_len), int(max_ctx_len), _DTYPE[q.dtype],
+        ctypes.c_void_p(stream)))
     return out
 
 

@@ -62,6 +62,7 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // is not an MFMA runs in fp32.
 // ---------------------------------------------------------------------------
 struct F16 {
+  static constexpr bool kSplitP = false;   // P in one f16 (11 significant bits) is exact enough
   static __device__ __forceinline__ f32x4 mfma_qk(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
@@ -80,6 +81,10 @@ struct F16 {
 };
 
 struct BF16 {
+  // P in one bf16 (8 significant bits) perturbs each weight by up to 2^-9: with a
+  // handful of keys that reaches the output almost undiluted, so P is carried as
+  // the sum of two bf16 values and multiplied into V by two MFMAs.
+  static constexpr bool kSplitP = true;
   static __device__ __forceinline__ f32x4 mfma_qk(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -250,6 +255,38 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Probabilities as P.V MFMA operands: p_e = 2^(x_e - m) for the lane's 4 keys,
+// rounded to the element type (to hi + lo, two values of it, with kSplitP; the
+// remainder p - hi is exact in fp32).  Returns the sum of the values the MFMAs use,
+// so the exp sum and the weighted sum share the same weights.
+template <class DT>
+__device__ __forceinline__ float prob_operands(const float (&x)[4], float m, u32x2& hi,
+                                               u32x2& lo) {
+  uint32_t h[4], l[4] = {0, 0, 0, 0};
+  float sum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float p = __builtin_amdgcn_exp2f(x[e] - m);
+    h[e] = DT::bits(p);
+    sum += DT::value(h[e]);
+    if constexpr (DT::kSplitP) {
+      l[e] = DT::bits(p - DT::value(h[e]));
+      sum += DT::value(l[e]);
+    }
+  }
+  hi = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  lo = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+  return sum;
+}
+
+// acc + V^T P^T for the probabilities of prob_operands.
+template <class DT>
+__device__ __forceinline__ f32x4 pv_mfma(u32x2 v, u32x2 hi, u32x2 lo, f32x4 acc) {
+  acc = DT::mfma_pv(v, hi, acc);
+  if constexpr (DT::kSplitP) acc = DT::mfma_pv(v, lo, acc);
+  return acc;
 }
 
 // A value every lane of the wave holds (read from LDS, say), moved to a scalar register.
@@ -567,15 +604,8 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& 
     const float m_new = fmaxf(m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
-    uint32_t pb[4];
-    float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pb[e] = DT::bits(__builtin_amdgcn_exp2f(x[e] - m_new));
-      psum += DT::value(pb[e]);          // sum the weights the MFMA actually uses
-    }
-    l_run = l_run * alpha + psum;
-    const u32x2 pop = {pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
+    u32x2 p_hi, p_lo;
+    l_run = l_run * alpha + prob_operands<DT>(x, m_new, p_hi, p_lo);
 
     // O^T[d, head] += sum_t V[t, d] P[head, t].  The A operand (lane: dim 16c + col,
     // tokens 4*grp .. +3) is V^T; ds_read_b64_tr_b16 transposes it out of the
@@ -599,7 +629,7 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& 
       u32x2 vop = __builtin_bit_cast(u32x2, raw);
       vop.x &= keep_lo;
       vop.y &= keep_hi;
-      acc[c] = DT::mfma_pv(vop, pop, acc[c] * alpha);
+      acc[c] = pv_mfma<DT>(vop, p_hi, p_lo, acc[c] * alpha);
     }
   }
 

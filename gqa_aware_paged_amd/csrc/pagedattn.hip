@@ -17,6 +17,7 @@
 #include <limits>
 
 #include "pa_kernels.h"
+#include "pa_prefill.h"
 
 #define PA_API extern "C" __attribute__((visibility("default")))
 
@@ -413,6 +414,77 @@ PA_API int paged_attn_workspace_init(void* workspace, size_t workspace_bytes,
   if (n == 0) return PA_OK;
   hipLaunchKernelGGL(pa::pa_zero_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
                      0, stream, static_cast<pa::u32x4*>(workspace), n);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+namespace {
+
+template <int D, class DT>
+void launch_prefill(const pa::PrefillArgs& args, unsigned grid, hipStream_t stream) {
+  hipLaunchKernelGGL((pa::pa_prefill_kernel<D, DT>), dim3(grid), dim3(pa::kPrefillWaves * 64),
+                     0, stream, args);
+}
+
+}  // namespace
+
+PA_API int paged_attn_prefill(void* out, const void* q, const void* k_new, const void* v_new,
+                              const void* key_cache, const void* value_cache,
+                              const int32_t* block_tables, const int32_t* ctx_lens,
+                              const int32_t* query_start, int num_seqs, int num_heads,
+                              int num_kv_heads, int head_dim, int block_size, float scale,
+                              int max_blocks_per_seq, int max_query_len, int max_ctx_len,
+                              int dtype, hipStream_t stream) {
+  int st = check_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       max_blocks_per_seq, max_ctx_len, 0, dtype);
+  if (st != PA_OK) return st;
+  if (!std::isfinite(scale) || max_query_len < 0 || max_ctx_len < 0) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !q || !k_new || !v_new || !key_cache || !value_cache || !block_tables ||
+      !ctx_lens || !query_start)
+    return PA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(out, 8) || !aligned(block_tables, 4) ||
+      !aligned(ctx_lens, 4) || !aligned(query_start, 4))
+    return PA_ERR_ALIGN;
+  const int G = num_heads / num_kv_heads;
+  const long long col_blocks =
+      (static_cast<long long>(max_query_len) * G + pa::kPrefillCols - 1) / pa::kPrefillCols;
+  const long long units = static_cast<long long>(num_seqs) * num_kv_heads;
+  const long long upx = (units + pa::kXcds - 1) / pa::kXcds;
+  const long long grid = pa::kXcds * upx * col_blocks;
+  if (grid > std::numeric_limits<int>::max() || col_blocks > std::numeric_limits<int>::max())
+    return PA_ERR_SHAPE;
+  pa::PrefillArgs args{};
+  args.out = out;
+  args.q = static_cast<const uint16_t*>(q);
+  args.k_new = static_cast<const uint16_t*>(k_new);
+  args.v_new = static_cast<const uint16_t*>(v_new);
+  args.kc = static_cast<const uint16_t*>(key_cache);
+  args.vc = static_cast<const uint16_t*>(value_cache);
+  args.bt = block_tables;
+  args.ctx_lens = ctx_lens;
+  args.qstart = query_start;
+  args.num_seqs = num_seqs;
+  args.num_heads = num_heads;
+  args.num_kv_heads = num_kv_heads;
+  args.group = G;
+  args.block_size = block_size;
+  args.max_blocks_per_seq = max_blocks_per_seq;
+  args.max_query_len = max_query_len;
+  args.max_ctx_len = max_ctx_len;
+  args.col_blocks = static_cast<int>(col_blocks);
+  args.units_per_xcd = static_cast<int>(upx);
+  args.scale_log2 = scale * kLog2e;
+  const unsigned g = static_cast<unsigned>(grid);
+  const bool f16 = dtype == PA_F16;
+  switch (head_dim) {
+    case 256: f16 ? launch_prefill<256, pa::F16>(args, g, stream)
+                  : launch_prefill<256, pa::BF16>(args, g, stream); break;
+    case 128: f16 ? launch_prefill<128, pa::F16>(args, g, stream)
+                  : launch_prefill<128, pa::BF16>(args, g, stream); break;
+    default: f16 ? launch_prefill<64, pa::F16>(args, g, stream)
+                 : launch_prefill<64, pa::BF16>(args, g, stream); break;
+  }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

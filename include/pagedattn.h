@@ -218,6 +218,39 @@ int paged_attn_decode_ex(void* out, const void* q, const void* key_cache,
                          size_t workspace_bytes, const pa_options* opt);
 
 /*
+ * Prefill over a paged context (the prefix path of the page of commit b80fd2b,
+ * paged_attn.py: one online softmax over the cached context gathered by block
+ * id, then over the current chunk under the causal mask).  For sequence s, the
+ * new tokens n = 0 .. Q-1, Q = query_start[s+1] - query_start[s], sit at rows
+ * r = query_start[s] + n of q, k_new and v_new; query head h of new token n
+ * attends to the ctx_lens[s] tokens in the paged caches (KV head
+ * h / (num_heads / num_kv_heads), as in decode) and to the new tokens j <= n:
+ *
+ *     out[r,h,:] = sum_u softmax_u(scale * q[r,h,:] . K_u) V_u
+ *
+ *   out                 [T][num_heads][head_dim] dtype, written (device); T = query_start[num_seqs]
+ *   q                   [T][num_heads][head_dim] dtype (device)
+ *   k_new, v_new        [T][num_kv_heads][head_dim] dtype (device): the chunk's own keys
+ *                       and values (not read from the caches)
+ *   key_cache/value_cache, block_tables   the paged context, layouts as for decode
+ *   ctx_lens            [num_seqs] int32 (device): cached tokens per sequence (<= 0: none;
+ *                       values above max_ctx_len are treated as max_ctx_len)
+ *   query_start         [num_seqs + 1] int32 (device), non-decreasing, query_start[0] = 0
+ *   max_query_len       host-known bound of the chunk lengths (sizes the grid; longer
+ *                       chunks are cut to it)
+ *   max_ctx_len         host-known bound of ctx_lens, <= max_blocks_per_seq*block_size
+ * Shapes, dtypes and alignment as for decode (k_new and v_new 16-byte aligned).
+ * No workspace.  Returns PA_OK or the first error found.
+ */
+int paged_attn_prefill(void* out, const void* q, const void* k_new, const void* v_new,
+                       const void* key_cache, const void* value_cache,
+                       const int32_t* block_tables, const int32_t* ctx_lens,
+                       const int32_t* query_start, int num_seqs, int num_heads,
+                       int num_kv_heads, int head_dim, int block_size, float scale,
+                       int max_blocks_per_seq, int max_query_len, int max_ctx_len, int dtype,
+                       hipStream_t stream);
+
+/*
  * Clears the ticket area (the first min(workspace_bytes,
  * PA_WORKSPACE_TICKET_BYTES) bytes) of a workspace with a kernel on `stream`, as
  * the fused combine (pa_options.fused_combine) needs before the first call on a

@@ -261,3 +261,31 @@ def test_workspace_init_validation(lib):
     assert lib.paged_attn_workspace_init(None, 0, stream) == 0          # nothing to clear
     assert lib.paged_attn_workspace_init(None, 4096, stream) == 1       # PA_ERR_NULL
     assert lib.paged_attn_workspace_init(ctypes.c_void_p(0x10010), 4096, stream) == 7
+
+
+def prefill_call(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, kn=FAKE, vn=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, qs=FAKE, S=2,
+             Hq=24, Hkv=4, D=256, bs=16, scale=0.0625, mbps=64, mq=128, mc=1024, dtype=0,
+             stream=None)
+    a.update(kw)
+    return lib.paged_attn_prefill(a["out"], a["q"], a["kn"], a["vn"], a["k"], a["v"], a["bt"],
+                                  a["cl"], a["qs"], a["S"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+                                  a["scale"], a["mbps"], a["mq"], a["mc"], a["dtype"],
+                                  a["stream"])
+
+
+def test_prefill_validation_errors_before_any_launch(lib):
+    """Every call here is rejected before a HIP call (or is an empty no-op)."""
+    assert prefill_call(lib, kn=None) == 1                  # PA_ERR_NULL
+    assert prefill_call(lib, qs=None) == 1
+    assert prefill_call(lib, Hkv=5) == 2                    # PA_ERR_SHAPE
+    assert prefill_call(lib, mc=64 * 16 + 1) == 2           # context longer than the table
+    assert prefill_call(lib, mq=-1) == 2
+    assert prefill_call(lib, scale=float("inf")) == 2
+    assert prefill_call(lib, D=96) == 3                     # PA_ERR_UNSUPPORTED
+    assert prefill_call(lib, bs=24) == 3
+    assert prefill_call(lib, dtype=5) == 3
+    assert prefill_call(lib, kn=ctypes.c_void_p(0x10008)) == 7   # PA_ERR_ALIGN
+    assert prefill_call(lib, out=ctypes.c_void_p(0x10004)) == 7
+    assert prefill_call(lib, S=0) == 0                      # nothing to do
+    assert prefill_call(lib, mq=0) == 0
