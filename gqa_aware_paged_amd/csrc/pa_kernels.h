@@ -178,10 +178,15 @@ __device__ __forceinline__ size_t tile_offset_in(int page, int t0, int kvh, int 
   return ((static_cast<size_t>(page) * Hkv + kvh) * bs + slot) * static_cast<size_t>(D);
 }
 
-// Page holding token t0 of sequence s (wave-uniform).
+// Page holding token t0 of sequence s (wave-uniform).  The table is read through
+// the constant address space: no kernel writes it, and a uniform index then
+// always becomes a scalar load, whose wait does not drain the vector loads (K/V
+// prefetches) issued before it.
 __device__ __forceinline__ int page_of(const int32_t* bt, int s, int t0, int bs, int mbps) {
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
   const unsigned blk = static_cast<unsigned>(t0) / static_cast<unsigned>(bs);
-  return __builtin_amdgcn_readfirstlane(bt[(size_t)s * mbps + blk]);
+  return __builtin_amdgcn_readfirstlane(
+      ((const_i32*)bt)[(size_t)s * mbps + blk]);
 }
 
 // A tile is read as two 8-token halves.  Pages holding the halves of the tile

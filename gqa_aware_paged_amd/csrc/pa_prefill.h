@@ -51,7 +51,10 @@ struct PrefillArgs {
   float scale_log2;
 };
 
-constexpr int kPrefillWaves = 4;
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 4
+#endif
+constexpr int kPrefillWaves = PA_PREFILL_WAVES;
 constexpr int kPrefillCols = 16 * kPrefillWaves;   // columns per workgroup
 constexpr int kXcds = 8;                           // MI355X: 8 XCDs, workgroups dealt round-robin
 
@@ -63,7 +66,7 @@ struct PrefillLds {
 };
 
 template <int D, class DT>
-__global__ __launch_bounds__(kPrefillWaves * 64, 2) void pa_prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void pa_prefill_kernel(PrefillArgs a) {
   constexpr int NT = kPrefillWaves * 64;
   constexpr int KS = D / 32;               // k-steps of the QK^T MFMA
   constexpr int DB = D / 16;               // 16-wide head_dim blocks of the PV MFMA
@@ -119,7 +122,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void pa_prefill_kernel(Prefi
   const int n_ctx_tiles = (C + kTile - 1) / kTile;
   const int n_tiles = n_ctx_tiles + n_hi / kTile + 1;
 
-  // cooperative tile load: thread tid owns chunks tid + NT*i of the K and V tiles
+  // cooperative tile load: thread tid owns chunks tid + NT*i of the K and V tiles.
+  // The index is clamped rather than guarded (head_dim 64 has fewer chunks than
+  // threads: the spare threads fetch and store the last chunk again, the same
+  // bytes to the same place), so the loads are unconditional and the registers
+  // they fill are not merged across branches, which would wait for them at once.
+  auto chunk = [&](int i) { return min(tid + NT * i, kTile * CH - 1); };
   u32x4 rk[CPT], rv[CPT];
   auto load = [&](int it, int2 pages) {
     if (it < n_ctx_tiles) {
@@ -128,39 +136,33 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void pa_prefill_kernel(Prefi
       tile_offsets(pages, t0, kvh, Hkv, bs, D, lo, hi);
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
-        const int c = tid + NT * i;
-        if (c < kTile * CH) {
-          const int row = c / CH, cc = c % CH;
-          const size_t off = (row < 8 ? lo : hi) + (size_t)(row % 8) * D + 8 * cc;
-          rk[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.kc + off));
-          rv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.vc + off));
-        }
+        const int c = chunk(i);
+        const int row = c / CH, cc = c % CH;
+        const size_t off = (row < 8 ? lo : hi) + (size_t)(row % 8) * D + 8 * cc;
+        rk[i] = *reinterpret_cast<const u32x4*>(a.kc + off);
+        rv[i] = *reinterpret_cast<const u32x4*>(a.vc + off);
       }
     } else {
       const int j0 = kTile * (it - n_ctx_tiles);
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
-        const int c = tid + NT * i;
-        if (c < kTile * CH) {
-          const int row = c / CH, cc = c % CH;
-          // rows past the chunk read its last row: finite, and masked by the causal rule
-          const int j = min(j0 + row, Qn - 1);
-          const size_t off = ((size_t)(r0 + j) * Hkv + kvh) * D + 8 * cc;
-          rk[i] = *reinterpret_cast<const u32x4*>(a.k_new + off);
-          rv[i] = *reinterpret_cast<const u32x4*>(a.v_new + off);
-        }
+        const int c = chunk(i);
+        const int row = c / CH, cc = c % CH;
+        // rows past the chunk read its last row: finite, and masked by the causal rule
+        const int j = min(j0 + row, Qn - 1);
+        const size_t off = ((size_t)(r0 + j) * Hkv + kvh) * D + 8 * cc;
+        rk[i] = *reinterpret_cast<const u32x4*>(a.k_new + off);
+        rv[i] = *reinterpret_cast<const u32x4*>(a.v_new + off);
       }
     }
   };
   auto stage = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = tid + NT * i;
-      if (c < kTile * CH) {
-        const int row = c / CH, cc = c % CH;
-        *reinterpret_cast<u32x4*>(sm.k[buf] + Z::byte_off(row, cc)) = rk[i];
-        *reinterpret_cast<u32x4*>(sm.v[buf] + ZV::byte_off(row, cc)) = rv[i];
-      }
+      const int c = chunk(i);
+      const int row = c / CH, cc = c % CH;
+      *reinterpret_cast<u32x4*>(sm.k[buf] + Z::byte_off(row, cc)) = rk[i];
+      *reinterpret_cast<u32x4*>(sm.v[buf] + ZV::byte_off(row, cc)) = rv[i];
     }
   };
   auto pages_of = [&](int it) {
