@@ -24,6 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0       # MI355X dense f16/bf16 MFMA
 COUNTERS = os.path.join(ROOT, "profiles", "pa_phase1_kernel_long-4x102400_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "gqa_aware_paged_amd", "csrc", f)
                   for f in ("pa_kernels.h", "pagedattn.hip")]
@@ -106,13 +107,92 @@ def cpu_baseline(w, nseqs: int):
             "seconds": dt, "us_per_step_extrapolated": dt * full * 1e6}
 
 
+def prefill_units(w):
+    """(new token, query head, key) triples of a prefill step: token n of a sequence
+    with C cached tokens sees C + n + 1 keys.  Each costs 4 * head_dim flop (the
+    q.k dot product and the p*v accumulation, a multiply and an add each)."""
+    keys = 0
+    for C, Q in zip(w.ctx.seq_lens_host.clip(0), w.q_lens_host):
+        keys += int(Q) * int(C) + int(Q) * (int(Q) + 1) // 2
+    return keys * w.ctx.num_heads
+
+
+def run_prefill(args, torch, pa, workloads):
+    """Chunked prefill over a paged context: one JSON line in TFLOP/s."""
+    import numpy as np
+    log("generating workload prefill")
+    w = workloads.prefill_chunk(device="cuda")
+    c = w.ctx
+    out = torch.empty_like(w.q)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        pa.prefill(w.q, w.k_new, w.v_new, c.key_cache, c.value_cache, c.block_tables,
+                   c.seq_lens, w.query_start, c.scale, w.max_q_len, c.max_seq_len, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    units = prefill_units(w)
+    flops = units * 4 * c.head_dim
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"timed {args.steps} steps: {ms * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s")
+    rec = {
+        "metric": "prefill attention TFLOP/s (causal chunk over a paged context), 1 GPU",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1e3, 2),
+        "timing": "hot", "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": c.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": c.num_seqs,
+                   "ctx_lens": f"all {int(c.seq_lens_host[0])}",
+                   "q_lens": f"all {int(w.q_lens_host[0])}", "num_heads": c.num_heads,
+                   "num_kv_heads": c.num_kv_heads, "head_dim": c.head_dim,
+                   "block_size": c.block_size, "parallelism": "single GPU"},
+        # the step is one launch of pa_prefill_kernel, timed with events on its stream
+        "roofline": {"bound": "mfma", "kernel": "pa_prefill_kernel", "achieved": round(tflops, 2),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": flops,
+                     "flops_per_unit": 4 * c.head_dim, "units_per_launch": units,
+                     "avg_launch_us": round(ms * 1e3, 2)},
+    }
+    if not args.no_cpu:
+        import oracle
+        # sample: every head of the first 32 new tokens of sequence 0 (each sees the
+        # whole cached context)
+        r0 = int(w.query_start_host[0])
+        rows = [(r0 + n, h) for n in range(32) for h in range(c.num_heads)]
+        t0 = time.perf_counter()
+        _, threads = oracle.prefill(w.q, w.k_new, w.v_new, c.key_cache, c.value_cache,
+                                    c.block_tables_host, c.seq_lens_host, w.query_start_host,
+                                    c.scale, c.dtype, rows=rows, return_threads=True)
+        dt = time.perf_counter() - t0
+        ctx0 = int(c.seq_lens_host[0])
+        sample_flops = sum((ctx0 + n + 1) for n in range(32)) * c.num_heads * 4 * c.head_dim
+        rec["cpu_baseline"] = {
+            "value": sample_flops / dt / 1e12, "unit": "TFLOP/s",
+            "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"32 new tokens x {c.num_heads} heads of sequence 0 ({dt:.2f} s), fp64 C "
+                      "oracle with OpenMP",
+            "seconds": dt}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long",
-                    choices=["tiny", "batch", "long", "mixed", "saturation"])
+                    choices=["tiny", "batch", "long", "mixed", "saturation", "prefill"])
     ap.add_argument("--partition-size", type=int, default=0,
                     help="tokens per partition; 0 = automatic (one workgroup per CU)")
     ap.add_argument("--p512", action="store_true",
@@ -153,6 +233,9 @@ def main():
     torch.cuda.set_device(dev)
     pa.lib()
 
+    if args.workload == "prefill":
+        run_prefill(args, torch, pa, workloads)
+        return
     log(f"generating workload {args.workload}")
     if args.workload == "long":
         w = workloads.long_context(device="cuda", head_dim=args.head_dim,

@@ -70,7 +70,7 @@ def _lib():
         lib.orc_partials.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, D, I, I, I]
         lib.orc_convert.argtypes = [P, P, ctypes.c_int64, I]
         lib.orc_prefill.argtypes = [P, P, I, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, D, I,
-                                    I]
+                                    I, P]
         for f in (lib.orc_decode, lib.orc_decode_rows, lib.orc_gather, lib.orc_partials,
                   lib.orc_prefill):
             f.restype = I
@@ -153,7 +153,7 @@ def decode_rows(rows: Sequence, q, key_cache, value_cache, block_tables, seq_len
 
 def prefill(q, k_new, v_new, key_cache, value_cache, block_tables, ctx_lens, query_start,
             scale: float, dtype: str, rows: Optional[Sequence] = None,
-            threads: int = 0) -> np.ndarray:
+            threads: int = 0, return_threads: bool = False):
     """fp64 prefill: q, k_new, v_new hold the new tokens of every sequence packed
     ([T, Hq, D] and [T, Hkv, D]; sequence s owns rows query_start[s] ..
     query_start[s+1]-1); ctx_lens[s] context tokens are in the paged caches.
@@ -172,10 +172,12 @@ def prefill(q, k_new, v_new, key_cache, value_cache, block_tables, ctx_lens, que
     else:
         r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 2))
         n, out = r.shape[0], np.empty((r.shape[0], D), np.float64)
+    used = ctypes.c_int(0)
     _check(_lib().orc_prefill(_p(out), None if r is None else _p(r), n, _p(qb), _p(knb),
                               _p(vnb), _p(kb), _p(vb), _p(bt), _p(cl), _p(qs), S, Hq, Hkv, D,
-                              bs, NB, MB, float(scale), DTYPE_CODE[dtype], int(threads)))
-    return out
+                              bs, NB, MB, float(scale), DTYPE_CODE[dtype], int(threads),
+                              ctypes.byref(used)))
+    return (out, used.value) if return_threads else out
 
 
 def gather(key_cache, value_cache, block_tables, seq_lens, Lcap: Optional[int] = None):

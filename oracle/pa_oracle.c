@@ -363,7 +363,7 @@ int orc_prefill(double* out, const int32_t* rows, int n_rows, const uint16_t* q,
                 const uint16_t* kn, const uint16_t* vn, const uint16_t* kc, const uint16_t* vc,
                 const int32_t* bt, const int32_t* ctx_lens, const int32_t* qstart, int S,
                 int Hq, int Hkv, int D, int bs, int NB, int MB, double scale, int dtype,
-                int nthreads) {
+                int nthreads, int* used_threads) {
     if (S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || NB < 0 || MB < 0) return -1;
     if (Hq % Hkv) return -1;
     if (qstart[0] != 0) return -1;
@@ -382,11 +382,16 @@ int orc_prefill(double* out, const int32_t* rows, int n_rows, const uint16_t* q,
         for (int r = qstart[s]; r < qstart[s + 1]; ++r) seq[r] = s;
     int64_t total = rows ? n_rows : (int64_t)T * Hq;
     int status = 0;
+    int used = 1;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
 #endif
 #pragma omp parallel
     {
+#ifdef _OPENMP
+#pragma omp single
+        used = omp_get_num_threads();
+#endif
         double* x = (double*)malloc(sizeof(double) * maxL);
         if (!x) {
 #pragma omp atomic write
@@ -413,5 +418,6 @@ int orc_prefill(double* out, const int32_t* rows, int n_rows, const uint16_t* q,
         free(x);
     }
     free(seq);
+    if (used_threads) *used_threads = used;
     return status;
 }
