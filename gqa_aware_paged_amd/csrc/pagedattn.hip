@@ -120,11 +120,14 @@ int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int 
   pl.balanced = P_req == 0 && !forced_tier && !uniform && !per_qhead &&
                 S <= pa::kMaxBalancedSeqs;
   if (pl.balanced) {
-    // shares x KV heads: about two resident workgroups per CU, but at least
+    // shares x KV heads: workgroups_per_cu resident workgroups per CU (measured on
+    // the batch and long workloads as for fixed partitions: one per CU at head_dim
+    // 256 with 16-token pages, 4% faster cold on the batch than two), but at least
     // kMinTilesPerWG tiles per workgroup
     const long long tiles = static_cast<long long>(S) * ((pl.max_seq_len + 15) / 16);
     long long ns = (tiles + kMinTilesPerWG - 1) / kMinTilesPerWG;
-    const long long ns_max = (2LL * cus) / Hkv > 0 ? (2LL * cus) / Hkv : 1;
+    const long long slots = static_cast<long long>(cus) * workgroups_per_cu(D, bs);
+    const long long ns_max = slots / Hkv > 0 ? slots / Hkv : 1;
     if (ns > ns_max) ns = ns_max;
     if (ns < 1) ns = 1;
     pl.num_wg = static_cast<int>(ns * Hkv);

@@ -183,7 +183,7 @@ size_t paged_attn_workspace_size_ex(int num_seqs, int num_heads, int num_kv_head
  *                       multiple of 16: the pages' fixed-partition grid), or 0:
  *                       automatic.  Automatic is the length-balanced split (the
  *                       step's tiles cut on the device into equal shares, one
- *                       workgroup per share and KV head, about two per CU) for up
+ *                       workgroup per share and KV head, w per CU as below) for up
  *                       to 1024 sequences; with equal lengths declared through
  *                       pa_options.total_tokens_hint, more sequences, or a forced
  *                       tier, it is fixed partitions of ceil(num_seqs *

@@ -96,7 +96,7 @@ def test_workspace_size_formula(lib):
     # explicit partitions: every sequence fits one partition -> one pass, no workspace
     assert lib.paged_attn_workspace_size(256, 24, 4, 256, 32, 512, 16384, 16384) == 0
     # balanced split (partition_size 0): two records per phase-1 workgroup + a job each
-    nw = 512
+    nw = 256
     recs = 2 * nw * 6
     acc = tickets + ((recs * 256 * 4 + 255) // 256) * 256
     ml = ((acc + recs * 8 + 255) // 256) * 256
@@ -149,16 +149,19 @@ def test_tier_thresholds(lib):
 
 
 def test_balanced_split_plan(lib):
-    """partition_size = 0: the step's tiles are cut into equal shares, two
-    workgroups per CU, whatever the length mix."""
+    """partition_size = 0: the step's tiles are cut into equal shares, one
+    workgroup per CU at head_dim 256 with 16-token pages (two otherwise), whatever
+    the length mix."""
     L = 102400
     info = pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0)          # 4 x 100K tokens
-    assert info["balanced"] == 1 and info["phase1_workgroups"] == 512
-    assert info["active_workgroups"] == 512 and info["partitioned_seqs"] == 4
-    assert info["phase2_workgroups"] == 512 * 2
-    # 1024 segments of 1024 tiles over 512 workgroups: shares end on segment ends
+    assert info["balanced"] == 1 and info["phase1_workgroups"] == 256
+    assert info["active_workgroups"] == 256 and info["partitioned_seqs"] == 4
+    assert info["phase2_workgroups"] == 256 * 2
+    assert pa.plan([L] * 4, 24, 4, 128, 16, L // 16, L, 0)["phase1_workgroups"] == 512
+    assert pa.plan([L] * 4, 24, 4, 256, 8, L // 8, L, 0)["phase1_workgroups"] == 512
+    # 1024 segments of 1024 tiles over 256 workgroups: shares end on segment ends
     info = pa.plan([16384] * 256, 24, 4, 256, 32, 512, 16384, 0)
-    assert info["phase1_workgroups"] == 512
+    assert info["phase1_workgroups"] == 256
     assert info["single_pass_seqs"] == 256 and info["partitioned_seqs"] == 0
     # short: one workgroup per 16 tiles of the length bound
     info = pa.plan([100] * 8, 24, 4, 256, 16, 8, 100, 0)

@@ -87,8 +87,8 @@ def test_batch_balanced():
 def test_empty_shares_inside_a_sequence():
     """Fewer tiles than shares: empty shares inside the long sequence add identity
     records, and each draws a ticket."""
-    say("case fused balanced, 67 tiles over 128 shares")
-    lens = [16] * 10 + [900]
+    say("case fused balanced, 48 tiles over 64 shares")
+    lens = [16] * 10 + [600]
     w = make(lens, max_blocks_per_seq=4096, partition_size=0, seed=41)
     info = pa.plan(lens, 24, 4, 256, 16, 4096, 65536, 0, fused_combine=True)
     assert info["balanced"] == 1 and info["fused"] == 1
