@@ -71,6 +71,11 @@ struct F16 {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
                                                  __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
   }
+  // 32 keys per instruction (the double-rate gfx950 form): A = V^T, B = P^T
+  static __device__ __forceinline__ f32x4 mfma_pv32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
   // round-to-nearest-even fp32 -> f16 bits
   static __device__ __forceinline__ uint32_t bits(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
@@ -92,6 +97,10 @@ struct BF16 {
   static __device__ __forceinline__ f32x4 mfma_pv(u32x2 a, u32x2 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
                                                      __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma_pv32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ uint32_t bits(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
@@ -294,11 +303,48 @@ __device__ __forceinline__ f32x4 pv_mfma(u32x2 v, u32x2 hi, u32x2 lo, f32x4 acc)
   return acc;
 }
 
+// pv_mfma over 32 keys with one double-rate MFMA per probability operand.
+template <class DT>
+__device__ __forceinline__ f32x4 pv_mfma32(u32x4 v, u32x4 hi, u32x4 lo, f32x4 acc) {
+  acc = DT::mfma_pv32(v, hi, acc);
+  if constexpr (DT::kSplitP) acc = DT::mfma_pv32(v, lo, acc);
+  return acc;
+}
+
 // A value every lane of the wave holds (read from LDS, say), moved to a scalar register.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-__device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shfl_xor(x, m, 64)); }
-__device__ __forceinline__ float xor_add(float x, int m) { return x + __shfl_xor(x, m, 64); }
+// The pair {x[l], x[l ^ M]} in lane l (M = 16 or 32), without LDS: v_permlane16_swap
+// (v_permlane32_swap) with x in both operands leaves x[l] in one result and x[l ^ M]
+// in the other; which is which differs between the two lanes of a pair, which
+// neither max nor + can see.
+template <int M>
+__device__ __forceinline__ void lane_pair(float x, float& a, float& b) {
+  static_assert(M == 16 || M == 32, "rows of 16 lanes or halves of the wave");
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  unsigned r0, r1;
+  if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    r0 = r[0], r1 = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    r0 = r[0], r1 = r[1];
+  }
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+template <int M>
+__device__ __forceinline__ float xor_max(float x) {
+  float a, b;
+  lane_pair<M>(x, a, b);
+  return fmaxf(a, b);
+}
+template <int M>
+__device__ __forceinline__ float xor_add(float x) {
+  float a, b;
+  lane_pair<M>(x, a, b);
+  return a + b;
+}
 
 // Merge of two compound partials (m, w, a): m is a base-2 max, w the weight sum
 // and a the weighted sum, both relative to m.  (-inf, 0, 0) is the identity.
@@ -604,8 +650,8 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& 
 #pragma unroll
     for (int e = 0; e < 4; ++e) x[e] = (tk + e < t_end) ? st[e] * a.scale_log2 : kNegInf;
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mx = xor_max(mx, 16);
-    mx = xor_max(mx, 32);
+    mx = xor_max<16>(mx);
+    mx = xor_max<32>(mx);
     const float m_new = fmaxf(m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
@@ -639,8 +685,8 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& 
   }
 
   // full exp sum of head `col` for this wave
-  l_run = xor_add(l_run, 16);
-  l_run = xor_add(l_run, 32);
+  l_run = xor_add<16>(l_run);
+  l_run = xor_add<32>(l_run);
 
   // merge the W wave states: waves 1..W-1 park (acc, m, l) in LDS, wave 0 combines
   __syncthreads();

@@ -9,14 +9,15 @@
 // the product is a real GEMM: a workgroup takes 64 "columns", a column being one
 // (new token, query head of the group) pair (column m = n*G + g), 16 per wave,
 // and streams the keys through them once:
-//   - each 16-token K/V tile (a context tile through the block table, or a tile of
-//     the chunk's own rows) is loaded cooperatively by the workgroup into
-//     double-buffered LDS, one barrier per tile;
-//   - each wave computes S^T = K_tile Q^T for its 16 columns with
-//     v_mfma_f32_16x16x32 (its Q^T operand stays in registers), the online
-//     softmax per column in base 2, and O^T += V^T P^T with v_mfma_f32_16x16x16
-//     (V^T read by ds_read_b64_tr_b16), exactly the decode tile step with query
-//     columns in place of query heads;
+//   - keys go in steps of 32 (two 16-token tiles: context tiles through the block
+//     table, or tiles of the chunk's own rows), loaded cooperatively by the
+//     workgroup into double-buffered LDS, one barrier per step;
+//   - each wave computes S^T = K Q^T for its 16 columns and the step's two tiles
+//     with v_mfma_f32_16x16x32 (its Q^T operand stays in registers), one online
+//     softmax update per column over the 32 keys in base 2, and O^T += V^T P^T
+//     with one double-rate v_mfma_f32_16x16x32 per 16 head dims (V^T of both
+//     tiles read by ds_read_b64_tr_b16): the decode tile step with query columns
+//     in place of query heads, its rescale spread over twice the keys;
 //   - the causal mask keeps key j for column (n, g) iff j <= n; tiles past a
 //     wave's last token are skipped, tiles past the workgroup's last token are
 //     not loaded.
@@ -58,11 +59,14 @@ constexpr int kPrefillWaves = PA_PREFILL_WAVES;
 constexpr int kPrefillCols = 16 * kPrefillWaves;   // columns per workgroup
 constexpr int kXcds = 8;                           // MI355X: 8 XCDs, workgroups dealt round-robin
 
+constexpr int kPrefillHalves = 2;                      // 16-token tiles per step
+constexpr int kPrefillStep = kTile * kPrefillHalves;   // keys per softmax step
+
 template <int D>
 struct PrefillLds {
-  static constexpr int kTileBytes = kTile * D * 2;
-  unsigned char k[2][kTileBytes];
-  unsigned char v[2][kTileBytes];
+  static constexpr int kStepBytes = kPrefillStep * D * 2;
+  unsigned char k[2][kStepBytes];
+  unsigned char v[2][kStepBytes];
 };
 
 template <int D, class DT>
@@ -71,8 +75,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void pa_pref
   constexpr int KS = D / 32;               // k-steps of the QK^T MFMA
   constexpr int DB = D / 16;               // 16-wide head_dim blocks of the PV MFMA
   constexpr int CH = D / 8;                // 16-byte chunks per row
-  constexpr int CPT = (kTile * CH + NT - 1) / NT;   // chunks per thread per tile (K or V)
-  constexpr int TILE_BYTES = PrefillLds<D>::kTileBytes;
+  constexpr int CPT = (kPrefillStep * CH + NT - 1) / NT;   // chunks per thread per step (K or V)
+  constexpr int HALF_BYTES = kTile * D * 2;                // one 16-token tile in LDS
   using Z = Swz<D>;
   using ZV = Swz<D, true>;
   __shared__ __attribute__((aligned(16))) PrefillLds<D> sm;
@@ -119,31 +123,35 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void pa_pref
   }
 
   const int bs = a.block_size, mbps = a.max_blocks_per_seq;
-  const int n_ctx_tiles = (C + kTile - 1) / kTile;
-  const int n_tiles = n_ctx_tiles + n_hi / kTile + 1;
+  const int n_ctx_steps = (C + kPrefillStep - 1) / kPrefillStep;
+  const int n_steps = n_ctx_steps + n_hi / kPrefillStep + 1;
 
-  // cooperative tile load: thread tid owns chunks tid + NT*i of the K and V tiles.
-  // The index is clamped rather than guarded (head_dim 64 has fewer chunks than
-  // threads: the spare threads fetch and store the last chunk again, the same
-  // bytes to the same place), so the loads are unconditional and the registers
-  // they fill are not merged across branches, which would wait for them at once.
-  auto chunk = [&](int i) { return min(tid + NT * i, kTile * CH - 1); };
+  // cooperative step load: thread tid owns chunks tid + NT*i of the K and V rows
+  // (row = chunk / CH: rows 0..15 are the first tile, 16..31 the second).  The
+  // index is clamped rather than guarded (spare threads, if any, fetch and store
+  // the last chunk again, the same bytes to the same place), so the loads are
+  // unconditional and the registers they fill are not merged across branches,
+  // which would wait for them at once.
+  auto chunk = [&](int i) { return min(tid + NT * i, kPrefillStep * CH - 1); };
   u32x4 rk[CPT], rv[CPT];
-  auto load = [&](int it, int2 pages) {
-    if (it < n_ctx_tiles) {
-      const int t0 = kTile * it;
-      size_t lo, hi;
-      tile_offsets(pages, t0, kvh, Hkv, bs, D, lo, hi);
+  auto load = [&](int it, int4 pages) {
+    if (it < n_ctx_steps) {
+      const int t0 = kPrefillStep * it;
+      size_t lo[2], hi[2];
+      tile_offsets(make_int2(pages.x, pages.y), t0, kvh, Hkv, bs, D, lo[0], hi[0]);
+      tile_offsets(make_int2(pages.z, pages.w), t0 + kTile, kvh, Hkv, bs, D, lo[1], hi[1]);
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
         const int c = chunk(i);
         const int row = c / CH, cc = c % CH;
-        const size_t off = (row < 8 ? lo : hi) + (size_t)(row % 8) * D + 8 * cc;
+        const int h = row / kTile, r = row % kTile;
+        const size_t base = r < 8 ? (h ? lo[1] : lo[0]) : (h ? hi[1] : hi[0]);
+        const size_t off = base + (size_t)(r % 8) * D + 8 * cc;
         rk[i] = *reinterpret_cast<const u32x4*>(a.kc + off);
         rv[i] = *reinterpret_cast<const u32x4*>(a.vc + off);
       }
     } else {
-      const int j0 = kTile * (it - n_ctx_tiles);
+      const int j0 = kPrefillStep * (it - n_ctx_steps);
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
         const int c = chunk(i);
@@ -165,11 +173,18 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void pa_pref
       *reinterpret_cast<u32x4*>(sm.v[buf] + ZV::byte_off(row, cc)) = rv[i];
     }
   };
+  // pages of the two tiles of a context step; a second tile wholly past the
+  // context (C not a multiple of 32) reads the first tile's pages again, at
+  // in-page slots, and every key of it is masked
   auto pages_of = [&](int it) {
-    return it < n_ctx_tiles ? tile_pages(a.bt, s, kTile * it, C, bs, mbps) : make_int2(0, 0);
+    if (it >= n_ctx_steps) return make_int4(0, 0, 0, 0);
+    const int t0 = kPrefillStep * it;
+    const int2 p0 = tile_pages(a.bt, s, t0, C, bs, mbps);
+    const int2 p1 = t0 + kTile < C ? tile_pages(a.bt, s, t0 + kTile, C, bs, mbps) : p0;
+    return make_int4(p0.x, p0.y, p1.x, p1.y);
   };
 
-  int2 pg_next = pages_of(1);
+  int4 pg_next = pages_of(1);
   load(0, pages_of(0));
   stage(0);
 
@@ -178,69 +193,89 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void pa_pref
 #pragma unroll
   for (int c = 0; c < DB; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int it = 0; it < n_tiles; ++it) {
+  for (int it = 0; it < n_steps; ++it) {
     const int buf = it & 1;
-    __syncthreads();                       // tile `it` staged; the other buffer is free
-    if (it + 1 < n_tiles) {
+    __syncthreads();                       // step `it` staged; the other buffer is free
+    if (it + 1 < n_steps) {
       load(it + 1, pg_next);
       pg_next = pages_of(it + 2);
     }
-    const bool ctx_tile = it < n_ctx_tiles;
-    const int u0 = ctx_tile ? kTile * it : kTile * (it - n_ctx_tiles);   // first key of the tile
-    if (wave_active && (ctx_tile || u0 <= wave_n_hi)) {
+    const bool ctx_step = it < n_ctx_steps;
+    const int u0 = kPrefillStep * (ctx_step ? it : it - n_ctx_steps);   // first key of the step
+    if (wave_active && (ctx_step || u0 <= wave_n_hi)) {
       const unsigned char* ldsK = sm.k[buf];
       const unsigned char* ldsV = sm.v[buf];
-      f32x4 st = {0.f, 0.f, 0.f, 0.f};
+      // S^T of the two tiles as two independent MFMA chains
+      f32x4 st[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 kop = *reinterpret_cast<const u32x4*>(ldsK + Z::byte_off(col, 4 * ks + grp));
-        st = DT::mfma_qk(kop, qop[ks], st);
-      }
-      // this lane holds column `col`, keys u0 + 4*grp + e
-      const int uk = u0 + 4 * grp;
-      float x[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool keep = ctx_tile ? uk + e < C : uk + e <= n_col;
-        x[e] = keep ? st[e] * a.scale_log2 : kNegInf;
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 kop = *reinterpret_cast<const u32x4*>(
+              ldsK + h * HALF_BYTES + Z::byte_off(col, 4 * ks + grp));
+          st[h] = DT::mfma_qk(kop, qop[ks], st[h]);
+        }
       }
-      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      mx = xor_max(mx, 16);
-      mx = xor_max(mx, 32);
-      // the first tile a column sees always holds one of its keys (context token 0,
-      // or new token 0 when there is no context), so m_new is finite from then on
+      // this lane holds column `col`, keys u0 + 16*h + 4*grp + e
+      float x[2][4];
+      float mx = kNegInf;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int uk = u0 + kTile * h + 4 * grp;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool keep = ctx_step ? uk + e < C : uk + e <= n_col;
+          x[h][e] = keep ? st[h][e] * a.scale_log2 : kNegInf;
+          mx = fmaxf(mx, x[h][e]);
+        }
+      }
+      mx = xor_max<16>(mx);
+      mx = xor_max<32>(mx);
+      // the first step a column sees always holds one of its keys (context token
+      // 0, or new token 0 when there is no context), so m_new is finite from then on
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
-      u32x2 p_hi, p_lo;
-      l_run = l_run * alpha + prob_operands<DT>(x, m_new, p_hi, p_lo);
+      u32x2 ph[2], pl[2];
+      const float sum0 = prob_operands<DT>(x[0], m_new, ph[0], pl[0]);
+      const float sum1 = prob_operands<DT>(x[1], m_new, ph[1], pl[1]);
+      l_run = l_run * alpha + (sum0 + sum1);
+      // B operand of the 16x16x32 MFMA: k = 8*grp + j is key 4*grp + j of the first
+      // tile for j < 4 and key 4*grp + j - 4 of the second for j >= 4; the V^T
+      // operand below takes its keys in the same order
+      const u32x4 p_hi = {ph[0].x, ph[0].y, ph[1].x, ph[1].y};
+      const u32x4 p_lo = {pl[0].x, pl[0].y, pl[1].x, pl[1].y};
       // context slots past C may hold anything (NaN): zero those V rows; chunk rows
       // past the causal limit are finite and weigh 0
-      uint32_t keep_lo = 0xffffffffu, keep_hi = 0xffffffffu;
-      if (ctx_tile && u0 + kTile > C) {
-        const int n = C - uk;
-        keep_lo = (n > 0 ? 0x0000ffffu : 0u) | (n > 1 ? 0xffff0000u : 0u);
-        keep_hi = (n > 2 ? 0x0000ffffu : 0u) | (n > 3 ? 0xffff0000u : 0u);
+      uint32_t keep[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+      if (ctx_step && u0 + kPrefillStep > C) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int n = C - (u0 + kTile * h + 4 * grp);
+          keep[2 * h] = (n > 0 ? 0x0000ffffu : 0u) | (n > 1 ? 0xffff0000u : 0u);
+          keep[2 * h + 1] = (n > 2 ? 0x0000ffffu : 0u) | (n > 3 ? 0xffff0000u : 0u);
+        }
       }
       const int vrow = 4 * grp + (col >> 2);
 #pragma unroll
       for (int c = 0; c < DB; ++c) {
         const int vcol = 16 * c + 4 * (col & 3);
         typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-        const i16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(ldsV + ZV::byte_off(vrow, vcol >> 3) + (vcol & 7) * 2));
-        u32x2 vop = __builtin_bit_cast(u32x2, raw);
-        vop.x &= keep_lo;
-        vop.y &= keep_hi;
-        acc[c] = pv_mfma<DT>(vop, p_hi, p_lo, acc[c] * alpha);
+        const unsigned char* vp = ldsV + ZV::byte_off(vrow, vcol >> 3) + (vcol & 7) * 2;
+        const i16x4 raw0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)vp);
+        const i16x4 raw1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + HALF_BYTES));
+        const u32x2 v0 = __builtin_bit_cast(u32x2, raw0);
+        const u32x2 v1 = __builtin_bit_cast(u32x2, raw1);
+        const u32x4 vop = {v0.x & keep[0], v0.y & keep[1], v1.x & keep[2], v1.y & keep[3]};
+        acc[c] = pv_mfma32<DT>(vop, p_hi, p_lo, acc[c] * alpha);
       }
     }
-    if (it + 1 < n_tiles) stage(buf ^ 1);
+    if (it + 1 < n_steps) stage(buf ^ 1);
   }
 
   // exp sum of the column over the 4 lane groups, then out = acc / l
-  l_run = xor_add(l_run, 16);
-  l_run = xor_add(l_run, 32);
+  l_run = xor_add<16>(l_run);
+  l_run = xor_add<32>(l_run);
   if (col_valid) {
     const float inv = 1.f / l_run;
     uint16_t* o = static_cast<uint16_t*>(a.out) +
