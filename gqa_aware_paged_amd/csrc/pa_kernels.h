@@ -63,6 +63,7 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // ---------------------------------------------------------------------------
 struct F16 {
   static constexpr bool kSplitP = false;   // P in one f16 (11 significant bits) is exact enough
+  static constexpr uint32_t kOnePair = 0x3C003C00u;   // two f16 ones
   static __device__ __forceinline__ f32x4 mfma_qk(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
@@ -90,6 +91,7 @@ struct BF16 {
   // handful of keys that reaches the output almost undiluted, so P is carried as
   // the sum of two bf16 values and multiplied into V by two MFMAs.
   static constexpr bool kSplitP = true;
+  static constexpr uint32_t kOnePair = 0x3F803F80u;   // two bf16 ones
   static __device__ __forceinline__ f32x4 mfma_qk(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -191,11 +193,12 @@ __device__ __forceinline__ size_t tile_offset_in(int page, int t0, int kvh, int 
 // the constant address space: no kernel writes it, and a uniform index then
 // always becomes a scalar load, whose wait does not drain the vector loads (K/V
 // prefetches) issued before it.
-__device__ __forceinline__ int page_of(const int32_t* bt, int s, int t0, int bs, int mbps) {
+__device__ __forceinline__ int page_at(const int32_t* bt, int s, int blk, int mbps) {
   typedef const __attribute__((address_space(4))) int32_t const_i32;
-  const unsigned blk = static_cast<unsigned>(t0) / static_cast<unsigned>(bs);
-  return __builtin_amdgcn_readfirstlane(
-      ((const_i32*)bt)[(size_t)s * mbps + blk]);
+  return __builtin_amdgcn_readfirstlane(((const_i32*)bt)[(size_t)s * mbps + blk]);
+}
+__device__ __forceinline__ int page_of(const int32_t* bt, int s, int t0, int bs, int mbps) {
+  return page_at(bt, s, static_cast<unsigned>(t0) / static_cast<unsigned>(bs), mbps);
 }
 
 // A tile is read as two 8-token halves.  Pages holding the halves of the tile

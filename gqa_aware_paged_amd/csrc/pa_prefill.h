@@ -44,6 +44,7 @@ struct PrefillArgs {
   int num_kv_heads;
   int group;
   int block_size;
+  int block_shift;           // log2(block_size) when a power of two, else -1
   int max_blocks_per_seq;
   int max_query_len;         // lengths are clamped to these bounds
   int max_ctx_len;
@@ -59,14 +60,32 @@ constexpr int kPrefillWaves = PA_PREFILL_WAVES;
 constexpr int kPrefillCols = 16 * kPrefillWaves;   // columns per workgroup
 constexpr int kXcds = 8;                           // MI355X: 8 XCDs, workgroups dealt round-robin
 
+// global-memory views (address space 1) for loads from a base held in SGPRs
+typedef const __attribute__((address_space(1))) unsigned char* gbytes;
+typedef const __attribute__((address_space(1))) u32x4 gu32x4;
+
 constexpr int kPrefillHalves = 2;                      // 16-token tiles per step
 constexpr int kPrefillStep = kTile * kPrefillHalves;   // keys per softmax step
 
+// The running max of a column moves only when a step's max exceeds it by more than
+// this (base 2): otherwise the step's probabilities are taken against the old max,
+// each at most 2^8 (well inside f16 and bf16), and the accumulators are not rescaled.
+constexpr float kRescaleLog2 = 8.f;
+
+// LDS of one step: 32 K rows, then 32 V rows, each row padded by 32 bytes so that
+// consecutive rows start 32 bytes apart modulo 256.  Measured with
+// SQ_LDS_BANK_CONFLICT on gfx950 (head_dim 256), that makes both MFMA operand
+// reads conflict-free without a swizzle: the 16-byte K reads of 16 rows, and the
+// transposed V reads (32 bytes of each of 4 rows per 16 lanes); a 16-byte pad
+// makes the K reads two-way conflicted.  With no swizzle, every read of a step is
+// one lane base plus an immediate offset.
 template <int D>
 struct PrefillLds {
-  static constexpr int kStepBytes = kPrefillStep * D * 2;
-  unsigned char k[2][kStepBytes];
-  unsigned char v[2][kStepBytes];
+  static constexpr int kKPitch = 2 * D + 32;
+  static constexpr int kVPitch = 2 * D + 32;
+  static constexpr int kKBytes = kPrefillStep * kKPitch;
+  static constexpr int kBufBytes = kKBytes + kPrefillStep * kVPitch;
+  unsigned char buf[2][kBufBytes];
 };
 
 template <int D, class DT>
@@ -76,10 +95,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void pa_pref
   constexpr int DB = D / 16;               // 16-wide head_dim blocks of the PV MFMA
   constexpr int CH = D / 8;                // 16-byte chunks per row
   constexpr int CPT = (kPrefillStep * CH + NT - 1) / NT;   // chunks per thread per step (K or V)
-  constexpr int HALF_BYTES = kTile * D * 2;                // one 16-token tile in LDS
-  using Z = Swz<D>;
-  using ZV = Swz<D, true>;
-  __shared__ __attribute__((aligned(16))) PrefillLds<D> sm;
+  using L = PrefillLds<D>;
+  __shared__ __attribute__((aligned(16))) L sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -122,76 +139,126 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void pa_pref
                           : u32x4{0, 0, 0, 0};
   }
 
-  const int bs = a.block_size, mbps = a.max_blocks_per_seq;
+  const int bs = a.block_size, mbps = a.max_blocks_per_seq, bsh = a.block_shift;
   const int n_ctx_steps = (C + kPrefillStep - 1) / kPrefillStep;
   const int n_steps = n_ctx_steps + n_hi / kPrefillStep + 1;
 
-  // cooperative step load: thread tid owns chunks tid + NT*i of the K and V rows
-  // (row = chunk / CH: rows 0..15 are the first tile, 16..31 the second).  The
-  // index is clamped rather than guarded (spare threads, if any, fetch and store
-  // the last chunk again, the same bytes to the same place), so the loads are
-  // unconditional and the registers they fill are not merged across branches,
-  // which would wait for them at once.
-  auto chunk = [&](int i) { return min(tid + NT * i, kPrefillStep * CH - 1); };
+  // Cooperative step load: thread tid owns chunks c = tid + NT*i of the K and V
+  // rows (row = c / CH: rows 0..15 are the first tile, 16..31 the second), so load
+  // i of every thread of a wave falls in one 8-row group (8*CH chunks), whose
+  // rows are contiguous in the cache; the address is that group's (wave-uniform)
+  // base plus a per-thread offset that does not change from step to step.
+  static_assert(CPT * NT == kPrefillStep * CH, "a step is a whole number of loads");
+  const unsigned lane_bytes = 16u * static_cast<unsigned>(tid % (8 * CH));
+  auto group_of = [&](int i) {
+    if constexpr (8 * CH == NT) return i;              // head_dim 256: load i is group i
+    else return i * (NT / (8 * CH)) + wave / (CH / 8);
+  };
+  // a (page, KV head) block of the cache is page_bytes long; the rows of KV head
+  // kvh start kvh_bytes into it (both below 2^32 for every supported shape)
+  const unsigned row_bytes = 2u * D;
+  const unsigned kvh_bytes = static_cast<unsigned>(kvh) * static_cast<unsigned>(bs) * row_bytes;
+  const unsigned page_bytes = static_cast<unsigned>(Hkv) * static_cast<unsigned>(bs) * row_bytes;
+  // Pages and in-page slots of the four 8-token groups of context step `it`
+  // (wave-uniform, one block-table division per step).  A group wholly past the
+  // context takes the previous group's page and slot: its rows are read again,
+  // in bounds, and masked.
+  struct StepPages { int page[4]; int slot[4]; };
+  auto pages_of = [&](int it) {
+    StepPages sp{};
+    if (it >= n_ctx_steps) return sp;
+    const int t0 = kPrefillStep * it;
+    int blk = bsh >= 0 ? t0 >> bsh : t0 / bs;
+    sp.page[0] = page_at(a.bt, s, blk, mbps);
+    sp.slot[0] = t0 - blk * bs;
+#pragma unroll
+    for (int g = 1; g < 4; ++g) {
+      sp.page[g] = sp.page[g - 1];
+      sp.slot[g] = sp.slot[g - 1];
+      if (t0 + 8 * g < C) {
+        if (sp.slot[g - 1] + 8 < bs) {
+          sp.slot[g] = sp.slot[g - 1] + 8;
+        } else {
+          sp.page[g] = page_at(a.bt, s, ++blk, mbps);
+          sp.slot[g] = 0;
+        }
+      }
+    }
+    return sp;
+  };
   u32x4 rk[CPT], rv[CPT];
-  auto load = [&](int it, int4 pages) {
+  auto load = [&](int it, const StepPages& sp) {
     if (it < n_ctx_steps) {
-      const int t0 = kPrefillStep * it;
-      size_t lo[2], hi[2];
-      tile_offsets(make_int2(pages.x, pages.y), t0, kvh, Hkv, bs, D, lo[0], hi[0]);
-      tile_offsets(make_int2(pages.z, pages.w), t0 + kTile, kvh, Hkv, bs, D, lo[1], hi[1]);
+      size_t off[4];                                   // byte offsets of the groups
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        off[g] = static_cast<size_t>(static_cast<unsigned>(sp.page[g])) * page_bytes +
+                 (kvh_bytes + static_cast<unsigned>(sp.slot[g]) * row_bytes);
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
-        const int c = chunk(i);
-        const int row = c / CH, cc = c % CH;
-        const int h = row / kTile, r = row % kTile;
-        const size_t base = r < 8 ? (h ? lo[1] : lo[0]) : (h ? hi[1] : hi[0]);
-        const size_t off = base + (size_t)(r % 8) * D + 8 * cc;
-        rk[i] = *reinterpret_cast<const u32x4*>(a.kc + off);
-        rv[i] = *reinterpret_cast<const u32x4*>(a.vc + off);
+        const int g = group_of(i);
+        const size_t o = g == 0 ? off[0] : g == 1 ? off[1] : g == 2 ? off[2] : off[3];
+        // the group's base stays a scalar pair and the lane offset a 32-bit value
+        // inside the loop, so each load takes the base + 32-bit offset form
+        gbytes kb = (gbytes)(a.kc) + o;
+        gbytes vb = (gbytes)(a.vc) + o;
+        unsigned lb = lane_bytes;
+        asm volatile("" : "+s"(kb), "+s"(vb), "+v"(lb));
+        rk[i] = *reinterpret_cast<const gu32x4*>(kb + lb);
+        rv[i] = *reinterpret_cast<const gu32x4*>(vb + lb);
       }
     } else {
       const int j0 = kPrefillStep * (it - n_ctx_steps);
+      const size_t base = ((size_t)(r0 + j0) * Hkv + kvh) * (size_t)(2 * D);
+      const int last = Qn - 1 - j0;                    // rows past it read row `last`
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
-        const int c = chunk(i);
+        const int c = tid + NT * i;
         const int row = c / CH, cc = c % CH;
-        // rows past the chunk read its last row: finite, and masked by the causal rule
-        const int j = min(j0 + row, Qn - 1);
-        const size_t off = ((size_t)(r0 + j) * Hkv + kvh) * D + 8 * cc;
-        rk[i] = *reinterpret_cast<const u32x4*>(a.k_new + off);
-        rv[i] = *reinterpret_cast<const u32x4*>(a.v_new + off);
+        const unsigned lb = static_cast<unsigned>((min(row, last) * Hkv * D + 8 * cc) * 2);
+        rk[i] = *reinterpret_cast<const u32x4*>(
+            reinterpret_cast<const unsigned char*>(a.k_new) + base + lb);
+        rv[i] = *reinterpret_cast<const u32x4*>(
+            reinterpret_cast<const unsigned char*>(a.v_new) + base + lb);
       }
     }
   };
-  auto stage = [&](int buf) {
+  // Staging into LDS.  V rows of context slots past C may hold anything (NaN) and
+  // are staged as zeros; their keys are masked out of the softmax as well.
+  auto stage = [&](int buf, int it) {
+    const int valid = it < n_ctx_steps ? C - kPrefillStep * it : kPrefillStep;
+    if (valid < kPrefillStep) {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+        if ((tid + NT * i) / CH >= valid) rv[i] = u32x4{0, 0, 0, 0};
+    }
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = chunk(i);
+      const int c = tid + NT * i;
       const int row = c / CH, cc = c % CH;
-      *reinterpret_cast<u32x4*>(sm.k[buf] + Z::byte_off(row, cc)) = rk[i];
-      *reinterpret_cast<u32x4*>(sm.v[buf] + ZV::byte_off(row, cc)) = rv[i];
+      *reinterpret_cast<u32x4*>(sm.buf[buf] + row * L::kKPitch + 16 * cc) = rk[i];
+      *reinterpret_cast<u32x4*>(sm.buf[buf] + L::kKBytes + row * L::kVPitch + 16 * cc) = rv[i];
     }
   };
-  // pages of the two tiles of a context step; a second tile wholly past the
-  // context (C not a multiple of 32) reads the first tile's pages again, at
-  // in-page slots, and every key of it is masked
-  auto pages_of = [&](int it) {
-    if (it >= n_ctx_steps) return make_int4(0, 0, 0, 0);
-    const int t0 = kPrefillStep * it;
-    const int2 p0 = tile_pages(a.bt, s, t0, C, bs, mbps);
-    const int2 p1 = t0 + kTile < C ? tile_pages(a.bt, s, t0 + kTile, C, bs, mbps) : p0;
-    return make_int4(p0.x, p0.y, p1.x, p1.y);
-  };
 
-  int4 pg_next = pages_of(1);
+  StepPages pg_next = pages_of(1);
   load(0, pages_of(0));
-  stage(0);
+  stage(0, 0);
 
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = kNegInf;
   f32x4 acc[DB];
 #pragma unroll
   for (int c = 0; c < DB; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // exp sums ride on the PV MFMA: a 17th A operand whose row 0 is all ones gives
+  // sum_k P[col][k] in row 0 of lsum (lanes with grp 0), from the same rounded
+  // probabilities as the weighted sum
+  f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t one2 = col == 0 ? DT::kOnePair : 0u;
+  const u32x4 ones = {one2, one2, one2, one2};
+
+  // lane bases of the LDS reads; everything else is an immediate offset
+  const int k_lane = col * L::kKPitch + 16 * grp;
+  const int v_lane = L::kKBytes + (4 * grp + (col >> 2)) * L::kVPitch + 8 * (col & 3);
 
   for (int it = 0; it < n_steps; ++it) {
     const int buf = it & 1;
@@ -203,8 +270,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void pa_pref
     const bool ctx_step = it < n_ctx_steps;
     const int u0 = kPrefillStep * (ctx_step ? it : it - n_ctx_steps);   // first key of the step
     if (wave_active && (ctx_step || u0 <= wave_n_hi)) {
-      const unsigned char* ldsK = sm.k[buf];
-      const unsigned char* ldsV = sm.v[buf];
+      const unsigned char* ldsK = sm.buf[buf] + k_lane;
+      const unsigned char* ldsV = sm.buf[buf] + v_lane;
       // S^T of the two tiles as two independent MFMA chains
       f32x4 st[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -212,70 +279,74 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void pa_pref
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const u32x4 kop = *reinterpret_cast<const u32x4*>(
-              ldsK + h * HALF_BYTES + Z::byte_off(col, 4 * ks + grp));
+              ldsK + h * kTile * L::kKPitch + 64 * ks);
           st[h] = DT::mfma_qk(kop, qop[ks], st[h]);
         }
       }
-      // this lane holds column `col`, keys u0 + 16*h + 4*grp + e
+      // this lane holds column `col`, keys u0 + 16*h + 4*grp + e; key u is kept iff
+      // u <= lim (u < C in the context, the causal rule in the chunk); a context
+      // step wholly inside the context needs no mask
       float x[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[h][e] = st[h][e] * a.scale_log2;
+      if (!ctx_step || u0 + kPrefillStep > C) {
+        const int lim = ctx_step ? C - 1 : n_col;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (u0 + kTile * h + 4 * grp + e > lim) x[h][e] = kNegInf;
+      }
       float mx = kNegInf;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int uk = u0 + kTile * h + 4 * grp;
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool keep = ctx_step ? uk + e < C : uk + e <= n_col;
-          x[h][e] = keep ? st[h][e] * a.scale_log2 : kNegInf;
-          mx = fmaxf(mx, x[h][e]);
-        }
-      }
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, x[h][e]);
       mx = xor_max<16>(mx);
       mx = xor_max<32>(mx);
-      // the first step a column sees always holds one of its keys (context token
-      // 0, or new token 0 when there is no context), so m_new is finite from then on
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+      // The first step a column sees always holds one of its keys (context token 0,
+      // or new token 0 when there is no context), so the first step of every lane
+      // moves the max to a finite value.  Later a wave rescales only when one of its
+      // columns' max grows by more than 2^kRescaleLog2.
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+#pragma unroll
+        for (int c = 0; c < DB; ++c) acc[c] *= alpha;
+        lsum *= alpha;
+      }
       u32x2 ph[2], pl[2];
-      const float sum0 = prob_operands<DT>(x[0], m_new, ph[0], pl[0]);
-      const float sum1 = prob_operands<DT>(x[1], m_new, ph[1], pl[1]);
-      l_run = l_run * alpha + (sum0 + sum1);
+      prob_operands<DT>(x[0], m_run, ph[0], pl[0]);
+      prob_operands<DT>(x[1], m_run, ph[1], pl[1]);
       // B operand of the 16x16x32 MFMA: k = 8*grp + j is key 4*grp + j of the first
       // tile for j < 4 and key 4*grp + j - 4 of the second for j >= 4; the V^T
       // operand below takes its keys in the same order
       const u32x4 p_hi = {ph[0].x, ph[0].y, ph[1].x, ph[1].y};
       const u32x4 p_lo = {pl[0].x, pl[0].y, pl[1].x, pl[1].y};
-      // context slots past C may hold anything (NaN): zero those V rows; chunk rows
-      // past the causal limit are finite and weigh 0
-      uint32_t keep[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
-      if (ctx_step && u0 + kPrefillStep > C) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int n = C - (u0 + kTile * h + 4 * grp);
-          keep[2 * h] = (n > 0 ? 0x0000ffffu : 0u) | (n > 1 ? 0xffff0000u : 0u);
-          keep[2 * h + 1] = (n > 2 ? 0x0000ffffu : 0u) | (n > 3 ? 0xffff0000u : 0u);
-        }
-      }
-      const int vrow = 4 * grp + (col >> 2);
+      // V^T of both tiles: lane (col, grp) of the transposed read supplies row
+      // 4*grp + col/4, columns 16c + 4*(col&3) .. +3
 #pragma unroll
       for (int c = 0; c < DB; ++c) {
-        const int vcol = 16 * c + 4 * (col & 3);
         typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-        const unsigned char* vp = ldsV + ZV::byte_off(vrow, vcol >> 3) + (vcol & 7) * 2;
+        const unsigned char* vp = ldsV + 32 * c;
         const i16x4 raw0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)vp);
-        const i16x4 raw1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + HALF_BYTES));
+        const i16x4 raw1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + kTile * L::kVPitch));
         const u32x2 v0 = __builtin_bit_cast(u32x2, raw0);
         const u32x2 v1 = __builtin_bit_cast(u32x2, raw1);
-        const u32x4 vop = {v0.x & keep[0], v0.y & keep[1], v1.x & keep[2], v1.y & keep[3]};
-        acc[c] = pv_mfma32<DT>(vop, p_hi, p_lo, acc[c] * alpha);
+        const u32x4 vop = {v0.x, v0.y, v1.x, v1.y};
+        acc[c] = pv_mfma32<DT>(vop, p_hi, p_lo, acc[c]);
       }
+      lsum = pv_mfma32<DT>(ones, p_hi, p_lo, lsum);
     }
-    if (it + 1 < n_steps) stage(buf ^ 1);
+    if (it + 1 < n_steps) stage(buf ^ 1, it + 1);
   }
 
-  // exp sum of the column over the 4 lane groups, then out = acc / l
-  l_run = xor_add<16>(l_run);
-  l_run = xor_add<32>(l_run);
+  // the column's exp sum from the lane of grp 0, then out = acc / l
+  const float l_run = __shfl(lsum[0], col, 64);
   if (col_valid) {
     const float inv = 1.f / l_run;
     uint16_t* o = static_cast<uint16_t*>(a.out) +

@@ -472,6 +472,7 @@ PA_API int paged_attn_prefill(void* out, const void* q, const void* k_new, const
   args.num_kv_heads = num_kv_heads;
   args.group = G;
   args.block_size = block_size;
+  args.block_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz(block_size) : -1;
   args.max_blocks_per_seq = max_blocks_per_seq;
   args.max_query_len = max_query_len;
   args.max_ctx_len = max_ctx_len;
