@@ -44,7 +44,8 @@ struct PrefillArgs {
   int num_kv_heads;
   int group;
   int block_size;
-  int block_shift;           // log2(block_size) when a power of two, else -1
+  unsigned bs_magic;         // t / block_size == umulhi(t, bs_magic) >> bs_shift, t < 2^31
+  int bs_shift;
   int max_blocks_per_seq;
   int max_query_len;         // lengths are clamped to these bounds
   int max_ctx_len;
@@ -88,7 +89,9 @@ struct PrefillLds {
   unsigned char buf[2][kBufBytes];
 };
 
-template <int D, class DT>
+// GPP: 8-token groups per page lookup, 1 for 8-token pages, else 2 (a 16-token tile
+// always lies in one page when the page size is a multiple of 16)
+template <int D, class DT, int GPP>
 __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void pa_prefill_kernel(PrefillArgs a) {
   constexpr int NT = kPrefillWaves * 64;
   constexpr int KS = D / 32;               // k-steps of the QK^T MFMA
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void pa_pref
                           : u32x4{0, 0, 0, 0};
   }
 
-  const int bs = a.block_size, mbps = a.max_blocks_per_seq, bsh = a.block_shift;
+  const int bs = a.block_size, mbps = a.max_blocks_per_seq;
   const int n_ctx_steps = (C + kPrefillStep - 1) / kPrefillStep;
   const int n_steps = n_ctx_steps + n_hi / kPrefillStep + 1;
 
@@ -159,30 +162,23 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void pa_pref
   const unsigned row_bytes = 2u * D;
   const unsigned kvh_bytes = static_cast<unsigned>(kvh) * static_cast<unsigned>(bs) * row_bytes;
   const unsigned page_bytes = static_cast<unsigned>(Hkv) * static_cast<unsigned>(bs) * row_bytes;
-  // Pages and in-page slots of the four 8-token groups of context step `it`
-  // (wave-uniform, one block-table division per step).  A group wholly past the
-  // context takes the previous group's page and slot: its rows are read again,
-  // in bounds, and masked.
-  struct StepPages { int page[4]; int slot[4]; };
+  // Pages and in-page slots of context step `it` (wave-uniform): one lookup per
+  // GPP 8-token groups, with no branch.  Token indices are clamped to the group
+  // (or tile) holding the last context token, so a step past the context, or a
+  // part of one, reads rows of that page again, in bounds, and masks them; the
+  // lookup for step it + 2 is issued a step ahead of its use.
+  constexpr int NL = 4 / GPP;
+  struct StepPages { int page[NL]; int slot[NL]; };
+  const int t_last = (C - 1) & ~(8 * GPP - 1);
   auto pages_of = [&](int it) {
     StepPages sp{};
-    if (it >= n_ctx_steps) return sp;
-    const int t0 = kPrefillStep * it;
-    int blk = bsh >= 0 ? t0 >> bsh : t0 / bs;
-    sp.page[0] = page_at(a.bt, s, blk, mbps);
-    sp.slot[0] = t0 - blk * bs;
+    if (C <= 0) return sp;
 #pragma unroll
-    for (int g = 1; g < 4; ++g) {
-      sp.page[g] = sp.page[g - 1];
-      sp.slot[g] = sp.slot[g - 1];
-      if (t0 + 8 * g < C) {
-        if (sp.slot[g - 1] + 8 < bs) {
-          sp.slot[g] = sp.slot[g - 1] + 8;
-        } else {
-          sp.page[g] = page_at(a.bt, s, ++blk, mbps);
-          sp.slot[g] = 0;
-        }
-      }
+    for (int j = 0; j < NL; ++j) {
+      const int t = min(kPrefillStep * it + 8 * GPP * j, t_last);
+      const int blk = static_cast<int>(__umulhi(static_cast<unsigned>(t), a.bs_magic) >> a.bs_shift);
+      sp.page[j] = page_at(a.bt, s, blk, mbps);
+      sp.slot[j] = t - blk * bs;
     }
     return sp;
   };
@@ -192,8 +188,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void pa_pref
       size_t off[4];                                   // byte offsets of the groups
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        off[g] = static_cast<size_t>(static_cast<unsigned>(sp.page[g])) * page_bytes +
-                 (kvh_bytes + static_cast<unsigned>(sp.slot[g]) * row_bytes);
+        off[g] = static_cast<size_t>(static_cast<unsigned>(sp.page[g / GPP])) * page_bytes +
+                 (kvh_bytes + static_cast<unsigned>(sp.slot[g / GPP] + 8 * (g % GPP)) * row_bytes);
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
         const int g = group_of(i);

@@ -424,8 +424,22 @@ namespace {
 
 template <int D, class DT>
 void launch_prefill(const pa::PrefillArgs& args, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((pa::pa_prefill_kernel<D, DT>), dim3(grid), dim3(pa::kPrefillWaves * 64),
-                     0, stream, args);
+  if (args.block_size == 8)
+    hipLaunchKernelGGL((pa::pa_prefill_kernel<D, DT, 1>), dim3(grid),
+                       dim3(pa::kPrefillWaves * 64), 0, stream, args);
+  else
+    hipLaunchKernelGGL((pa::pa_prefill_kernel<D, DT, 2>), dim3(grid),
+                       dim3(pa::kPrefillWaves * 64), 0, stream, args);
+}
+
+// Division by the page size as a multiply-high and a shift (Granlund-Montgomery
+// with a 31-bit dividend): with k = ceil(log2 bs) and m = floor(2^(31+k) / bs) + 1
+// (below 2^32), t / bs == (t * m) >> (31 + k) for every 0 <= t < 2^31.
+void page_divider(int bs, unsigned& magic, int& shift) {
+  int k = 0;
+  while ((1LL << k) < bs) ++k;
+  magic = static_cast<unsigned>((1ULL << (31 + k)) / static_cast<unsigned long long>(bs) + 1);
+  shift = k - 1;
 }
 
 }  // namespace
@@ -472,7 +486,7 @@ PA_API int paged_attn_prefill(void* out, const void* q, const void* k_new, const
   args.num_kv_heads = num_kv_heads;
   args.group = G;
   args.block_size = block_size;
-  args.block_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz(block_size) : -1;
+  page_divider(block_size, args.bs_magic, args.bs_shift);
   args.max_blocks_per_seq = max_blocks_per_seq;
   args.max_query_len = max_query_len;
   args.max_ctx_len = max_ctx_len;
