@@ -61,6 +61,10 @@ constexpr int kPrefillWaves = PA_PREFILL_WAVES;
 constexpr int kPrefillCols = 16 * kPrefillWaves;   // columns per workgroup
 constexpr int kXcds = 8;                           // MI355X: 8 XCDs, workgroups dealt round-robin
 
+// The two phases of a workgroup's key loop: the cached context, then the chunk.
+template <bool kCtx>
+struct PrefillPhase { static constexpr bool ctx = kCtx; };
+
 // global-memory views (address space 1) for loads from a base held in SGPRs
 typedef const __attribute__((address_space(1))) unsigned char* gbytes;
 typedef const __attribute__((address_space(1))) u32x4 gu32x4;
@@ -182,9 +186,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void pa_pref
     }
     return sp;
   };
-  u32x4 rk[CPT], rv[CPT];
-  auto load = [&](int it, const StepPages& sp) {
-    if (it < n_ctx_steps) {
+  struct Regs { u32x4 k[CPT], v[CPT]; };
+  auto load = [&](auto phase, int it, StepPages sp, Regs& r) {
+    if constexpr (decltype(phase)::ctx) {
       size_t off[4];                                   // byte offsets of the groups
 #pragma unroll
       for (int g = 0; g < 4; ++g)
@@ -200,8 +204,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void pa_pref
         gbytes vb = (gbytes)(a.vc) + o;
         unsigned lb = lane_bytes;
         asm volatile("" : "+s"(kb), "+s"(vb), "+v"(lb));
-        rk[i] = *reinterpret_cast<const gu32x4*>(kb + lb);
-        rv[i] = *reinterpret_cast<const gu32x4*>(vb + lb);
+        r.k[i] = *reinterpret_cast<const gu32x4*>(kb + lb);
+        r.v[i] = *reinterpret_cast<const gu32x4*>(vb + lb);
       }
     } else {
       const int j0 = kPrefillStep * (it - n_ctx_steps);
@@ -212,34 +216,32 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void pa_pref
         const int c = tid + NT * i;
         const int row = c / CH, cc = c % CH;
         const unsigned lb = static_cast<unsigned>((min(row, last) * Hkv * D + 8 * cc) * 2);
-        rk[i] = *reinterpret_cast<const u32x4*>(
+        r.k[i] = *reinterpret_cast<const u32x4*>(
             reinterpret_cast<const unsigned char*>(a.k_new) + base + lb);
-        rv[i] = *reinterpret_cast<const u32x4*>(
+        r.v[i] = *reinterpret_cast<const u32x4*>(
             reinterpret_cast<const unsigned char*>(a.v_new) + base + lb);
       }
     }
   };
   // Staging into LDS.  V rows of context slots past C may hold anything (NaN) and
   // are staged as zeros; their keys are masked out of the softmax as well.
-  auto stage = [&](int buf, int it) {
-    const int valid = it < n_ctx_steps ? C - kPrefillStep * it : kPrefillStep;
-    if (valid < kPrefillStep) {
+  auto stage = [&](auto phase, unsigned char* dst, int it, Regs& r) {
+    if constexpr (decltype(phase)::ctx) {
+      const int valid = C - kPrefillStep * it;
+      if (valid < kPrefillStep) {
 #pragma unroll
-      for (int i = 0; i < CPT; ++i)
-        if ((tid + NT * i) / CH >= valid) rv[i] = u32x4{0, 0, 0, 0};
+        for (int i = 0; i < CPT; ++i)
+          if ((tid + NT * i) / CH >= valid) r.v[i] = u32x4{0, 0, 0, 0};
+      }
     }
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + NT * i;
       const int row = c / CH, cc = c % CH;
-      *reinterpret_cast<u32x4*>(sm.buf[buf] + row * L::kKPitch + 16 * cc) = rk[i];
-      *reinterpret_cast<u32x4*>(sm.buf[buf] + L::kKBytes + row * L::kVPitch + 16 * cc) = rv[i];
+      *reinterpret_cast<u32x4*>(dst + row * L::kKPitch + 16 * cc) = r.k[i];
+      *reinterpret_cast<u32x4*>(dst + L::kKBytes + row * L::kVPitch + 16 * cc) = r.v[i];
     }
   };
-
-  StepPages pg_next = pages_of(1);
-  load(0, pages_of(0));
-  stage(0, 0);
 
   float m_run = kNegInf;
   f32x4 acc[DB];
@@ -256,18 +258,14 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void pa_pref
   const int k_lane = col * L::kKPitch + 16 * grp;
   const int v_lane = L::kKBytes + (4 * grp + (col >> 2)) * L::kVPitch + 8 * (col & 3);
 
-  for (int it = 0; it < n_steps; ++it) {
-    const int buf = it & 1;
-    __syncthreads();                       // step `it` staged; the other buffer is free
-    if (it + 1 < n_steps) {
-      load(it + 1, pg_next);
-      pg_next = pages_of(it + 2);
-    }
-    const bool ctx_step = it < n_ctx_steps;
+  // one step of every wave: S^T, the online softmax and O^T += V^T P^T over the
+  // 32 keys of step `it`, read from the LDS buffer at `lds`
+  auto compute = [&](auto phase, int it, const unsigned char* lds) {
+    constexpr bool ctx_step = decltype(phase)::ctx;
     const int u0 = kPrefillStep * (ctx_step ? it : it - n_ctx_steps);   // first key of the step
     if (wave_active && (ctx_step || u0 <= wave_n_hi)) {
-      const unsigned char* ldsK = sm.buf[buf] + k_lane;
-      const unsigned char* ldsV = sm.buf[buf] + v_lane;
+      const unsigned char* ldsK = lds + k_lane;
+      const unsigned char* ldsV = lds + v_lane;
       // S^T of the two tiles as two independent MFMA chains
       f32x4 st[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -338,8 +336,49 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void pa_pref
       }
       lsum = pv_mfma32<DT>(ones, p_hi, p_lo, lsum);
     }
-    if (it + 1 < n_steps) stage(buf ^ 1, it + 1);
-  }
+  };
+
+  // Software pipeline, two steps deep, run once over the context steps and once
+  // over the chunk steps (each phase with a single load path, so the compiler's
+  // waits before a staging cover exactly the older register set).  The loads of
+  // step it + 2 are issued at the top of step it into the register set freed when
+  // step it was staged, and land while steps it and it + 1 are computed; step
+  // it + 1 is staged from the other set at the end of step it.  Unrolled by two so
+  // that register sets and LDS buffers are fixed at each point.  Every prefetch is
+  // issued, one past the phase's end reading its last step again (in bounds, never
+  // staged); block-table lookups run a step ahead of the loads that use them.
+  auto run = [&](auto phase, int first, int end) {
+    constexpr bool kCtx = decltype(phase)::ctx;
+    auto pages = [&](int it) {
+      if constexpr (kCtx) return pages_of(it);
+      else return StepPages{};
+    };
+    auto prefetch = [&](int it, StepPages sp, Regs& r) {
+      load(phase, min(it, end - 1), sp, r);
+    };
+    Regs ra, rb;
+    prefetch(first, pages(first), ra);
+    prefetch(first + 1, pages(first + 1), rb);
+    StepPages pg_next = pages(first + 2);
+    stage(phase, sm.buf[0], first, ra);
+    for (int it = first; it < end; it += 2) {
+      __syncthreads();                     // step it staged in buffer 0; buffer 1 free
+      prefetch(it + 2, pg_next, ra);
+      pg_next = pages(it + 3);
+      compute(phase, it, sm.buf[0]);
+      if (it + 1 < end) {
+        stage(phase, sm.buf[1], it + 1, rb);
+        __syncthreads();                   // step it + 1 staged in buffer 1; buffer 0 free
+        prefetch(it + 3, pg_next, rb);
+        pg_next = pages(it + 4);
+        compute(phase, it + 1, sm.buf[1]);
+        if (it + 2 < end) stage(phase, sm.buf[0], it + 2, ra);
+      }
+    }
+  };
+  if (n_ctx_steps > 0) run(PrefillPhase<true>{}, 0, n_ctx_steps);
+  __syncthreads();                         // both buffers free before the chunk phase
+  run(PrefillPhase<false>{}, n_ctx_steps, n_steps);
 
   // the column's exp sum from the lane of grp 0, then out = acc / l
   const float l_run = __shfl(lsum[0], col, 64);
