@@ -159,7 +159,7 @@ def test_head_shapes(D, heads, tier):
     assert_close(gpu_out(out), oracle_full(w), f"Hq{Hq}/Hkv{Hkv}/D{D}/{tier}")
 
 
-@pytest.mark.parametrize("bs", [8, 16])
+@pytest.mark.parametrize("bs", [8, 16, 48])
 @pytest.mark.parametrize("tier", ["single", "partitioned", "balanced"])
 def test_edge_lengths(tier, bs):
     lens = [0, 1, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1023, 1024, 1025,

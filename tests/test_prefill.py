@@ -44,7 +44,7 @@ def ref(w, rows=None):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("bs", [8, 16, 32, 48, 64, 80])
 def test_small_mixed(dtype, bs):
     say(f"case prefill small dtype={dtype} bs={bs}")
     w = make([0, 1, 15, 16, 17, 100, 333], [1, 7, 16, 17, 40, 3, 65], dtype=dtype,
@@ -60,6 +60,19 @@ def test_head_shapes(D, heads):
     w = make([50, 0, 260], [20, 33, 9], num_heads=Hq, num_kv_heads=Hkv, head_dim=D,
              scale=1 / math.sqrt(D), dtype="bf16" if Hq == 64 else "f16", seed=52 + D + Hq)
     assert_close(gpu_out(run(w)), ref(w), f"prefill/D{D}/{Hq}x{Hkv}")
+
+
+@pytest.mark.parametrize("bs", [16, 48])
+def test_step_boundaries(bs):
+    """Context and chunk lengths on both sides of the 32-key steps: one to four
+    context steps and one to four chunk steps, odd and even counts in both phases
+    of the two-deep pipeline, context tails that leave the second tile of a step
+    empty or partial."""
+    ctx = [32, 33, 64, 65, 96, 97, 128, 16, 15, 1]
+    ql = [32, 33, 64, 65, 96, 1, 2, 31, 97, 128]
+    say(f"case prefill step boundaries bs={bs}")
+    w = make(ctx, ql, block_size=bs, seed=58 + bs)
+    assert_close(gpu_out(run(w)), ref(w), f"prefill/steps/bs{bs}")
 
 
 def test_long_chunk_many_column_blocks():
