@@ -10,16 +10,18 @@
 // (new token, query head of the group) pair (column m = n*G + g), 16 per wave,
 // and streams the keys through them once:
 //   - keys go in steps of 32 (two 16-token tiles: context tiles through the block
-//     table, or tiles of the chunk's own rows), loaded cooperatively by the
-//     workgroup into double-buffered LDS, one barrier per step;
+//     table, then tiles of the chunk's own rows), loaded cooperatively by the
+//     workgroup two steps ahead into registers and staged into double-buffered
+//     LDS, one barrier per step;
 //   - each wave computes S^T = K Q^T for its 16 columns and the step's two tiles
 //     with v_mfma_f32_16x16x32 (its Q^T operand stays in registers), one online
 //     softmax update per column over the 32 keys in base 2, and O^T += V^T P^T
 //     with one double-rate v_mfma_f32_16x16x32 per 16 head dims (V^T of both
-//     tiles read by ds_read_b64_tr_b16): the decode tile step with query columns
-//     in place of query heads, its rescale spread over twice the keys;
-//   - the causal mask keeps key j for column (n, g) iff j <= n; tiles past a
-//     wave's last token are skipped, tiles past the workgroup's last token are
+//     tiles read by ds_read_b64_tr_b16), plus one for the exp sums: the decode
+//     tile step with query columns in place of query heads, the accumulator
+//     rescaled only when a column's max grows by more than 2^8;
+//   - the causal mask keeps key j for column (n, g) iff j <= n; steps past a
+//     wave's last token are skipped, steps past the workgroup's last token are
 //     not loaded.
 // The grid is XCD-aware: every column block of one (sequence, KV head) runs on
 // the same XCD, so their repeated reads of its K/V hit that XCD's L2.
@@ -50,7 +52,6 @@ struct PrefillArgs {
   int max_query_len;         // lengths are clamped to these bounds
   int max_ctx_len;
   int col_blocks;            // column blocks per (sequence, KV head)
-  int units_per_xcd;         // (sequence, KV head) units per XCD
   float scale_log2;
 };
 

@@ -491,7 +491,6 @@ PA_API int paged_attn_prefill(void* out, const void* q, const void* k_new, const
   args.max_query_len = max_query_len;
   args.max_ctx_len = max_ctx_len;
   args.col_blocks = static_cast<int>(col_blocks);
-  args.units_per_xcd = static_cast<int>(upx);
   args.scale_log2 = scale * kLog2e;
   const unsigned g = static_cast<unsigned>(grid);
   const bool f16 = dtype == PA_F16;
