@@ -3,8 +3,10 @@
 
 A step is one paged_attn_decode call over the whole batch (phase 1 with the
 tier dispatch, then phase 2).  The default workload is long-context decode:
-4 sequences x 102400 tokens (200 partitions of 512), 24 query / 4 KV heads,
-head_dim 256, 16-token pages, fp16, q = 8 N(0,1) so the softmax is peaked.
+4 sequences x 102400 tokens (automatic partitions: 16 of 6400 tokens, one
+workgroup per CU), 24 query / 4 KV heads, head_dim 256, 16-token pages, fp16,
+q = 8 N(0,1) so the softmax is peaked.  `--workload prefill` times the chunked
+prefill kernel instead (TFLOP/s).
 
 Prints one JSON line.  `value` is the effective KV-cache read bandwidth of the
 whole step (sum of seq_len x KV heads x head_dim x 2 bytes x 2 (K and V),
@@ -121,7 +123,8 @@ def run_prefill(args, torch, pa, workloads):
     """Chunked prefill over a paged context: one JSON line in TFLOP/s."""
     import numpy as np
     log("generating workload prefill")
-    w = workloads.prefill_chunk(device="cuda")
+    w = workloads.prefill_chunk(device="cuda", head_dim=args.head_dim, dtype=args.dtype,
+                                block_size=args.block_size)
     c = w.ctx
     out = torch.empty_like(w.q)
     stream = torch.cuda.current_stream()
@@ -203,9 +206,11 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="merge partitions inside phase 1 (atomic ticket) instead of a phase-2 launch")
     ap.add_argument("--head-dim", type=int, default=256,
-                    help="long workload only: head_dim for shape sweeps")
+                    help="long and prefill workloads only: head_dim for shape sweeps")
     ap.add_argument("--block-size", type=int, default=16,
-                    help="long workload only: block_size for shape sweeps")
+                    help="long and prefill workloads only: block_size for shape sweeps")
+    ap.add_argument("--dtype", default="f16", choices=["f16", "bf16"],
+                    help="prefill workload only: element type")
     ap.add_argument("--no-hint", action="store_true",
                     help="do not pass the host-side total of seq_lens to the planner")
     ap.add_argument("--num-cus", type=int, default=0,
@@ -220,6 +225,10 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decode path runs on a single MI355X and has no "
               "multi-GPU mode; use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.dtype != "f16" and args.workload != "prefill":
+        print("--dtype applies to the prefill workload only; the decode workloads are f16",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -342,13 +342,16 @@ def make_prefill(name: str, ctx_lens: Sequence[int], q_lens: Sequence[int],
 
 
 def prefill_chunk(device="cpu", poison=False, seed=1006, num_seqs=4, ctx_len=16384,
-                  q_len=2048):
+                  q_len=2048, head_dim=256, dtype="f16", block_size=16):
     """Chunked prefill: 4 sequences with 16384 cached context tokens each and a
     2048-token new chunk, 24/4 heads, head_dim 256, 16-token pages, f16 N(0,1),
-    scale 1/16."""
-    return make_prefill(f"prefill-{num_seqs}x({ctx_len}+{q_len})", [ctx_len] * num_seqs,
-                        [q_len] * num_seqs, scale=1.0 / 16, seed=seed, device=device,
-                        poison=poison)
+    scale 1/sqrt(head_dim) (1/16); head_dim, dtype and block_size can be varied."""
+    name = f"prefill-{num_seqs}x({ctx_len}+{q_len})"
+    if (head_dim, dtype, block_size) != (256, "f16", 16):
+        name += f"-D{head_dim}-{dtype}-bs{block_size}"
+    return make_prefill(name, [ctx_len] * num_seqs, [q_len] * num_seqs, head_dim=head_dim,
+                        block_size=block_size, dtype=dtype, scale=1.0 / math.sqrt(head_dim),
+                        seed=seed, device=device, poison=poison)
 
 
 NAMED = {"tiny": tiny, "batch": batch, "long": long_context, "mixed": mixed,
