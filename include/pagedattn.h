@@ -188,7 +188,7 @@ size_t paged_attn_workspace_size_ex(int num_seqs, int num_heads, int num_kv_head
  *                       pa_options.total_tokens_hint, more sequences, or a forced
  *                       tier, it is fixed partitions of ceil(num_seqs *
  *                       max_seq_len * num_kv_heads / (256 * w)) tokens rounded up
- *                       to 16, at least 256 and at most max_seq_len, where w (the
+ *                       to 16, at least 64 and at most max_seq_len, where w (the
  *                       resident workgroups per CU aimed at) is 1 for head_dim 256
  *                       with block_size >= 16 and 2 otherwise
  *   workspace           device scratch of workspace_bytes bytes (may be NULL when

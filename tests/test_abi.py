@@ -163,9 +163,9 @@ def test_balanced_split_plan(lib):
     info = pa.plan([16384] * 256, 24, 4, 256, 32, 512, 16384, 0)
     assert info["phase1_workgroups"] == 256
     assert info["single_pass_seqs"] == 256 and info["partitioned_seqs"] == 0
-    # short: one workgroup per 16 tiles of the length bound
+    # short: one workgroup per 4 tiles (one per wave) of the length bound
     info = pa.plan([100] * 8, 24, 4, 256, 16, 8, 100, 0)
-    assert info["phase1_workgroups"] == 4 * ((8 * 7 + 15) // 16)   # shares x KV heads
+    assert info["phase1_workgroups"] == 4 * ((8 * 7 + 3) // 4)   # shares x KV heads
     # a mix of very short and very long sequences: the long ones are cut into many
     # shares; a short one is cut only where a share boundary happens to fall in it
     lens = [64] * 60 + [65536] * 4
