@@ -150,6 +150,8 @@ struct DecodeArgs {
   int single_pass_max_len;  // grid mode
   int max_parts;            // grid mode
   int num_wg;               // balanced mode: workgroups of phase 1
+  int xcd_skew;             // XCD-paired shares: permille the even-XCD member of a pair
+                            // takes above the mean (0: equal shares), see xcd_cut
   float scale_log2;         // scale * log2(e)
 };
 
@@ -171,6 +173,30 @@ struct GatherArgs {
 #define PA_MAX_BALANCED_SEQS 1024
 #endif
 constexpr int kMaxBalancedSeqs = PA_MAX_BALANCED_SEQS;   // balanced mode keeps a prefix of seq_lens in LDS
+
+// XCD-paired shares.  The hardware hands out workgroup i to XCD i mod 8, and on
+// MI355X the workgroups of the odd XCDs stream K/V ~8-10% slower than those of
+// the even ones (measured per workgroup with the 100 MHz wall clock: same
+// bytes, same pages, any assignment of KV heads to XCDs), so with equal shares
+// the odd XCDs finish last.  Shares therefore come in pairs whose members run
+// on workgroups of opposite parity, and the even one takes (1000 + skew)/1000 of
+// the pair's mean.  share_cut(T, j, NS, skew) is the first item of share j of NS
+// shares of T items in that scheme (pairs (2i, 2i+1), an odd last share alone);
+// skew 0 gives T*j/NS.  Exact integer arithmetic, used by the planner too.
+__host__ __device__ __forceinline__ long long share_cut(long long T, long long j, long long NS,
+                                                        int skew) {
+  if (j >= NS) return T;
+  return T * (1000 * j + skew * (j & 1)) / (1000 * NS);
+}
+
+// Share holding item t < T: the largest j with share_cut(j) <= t.
+__host__ __device__ __forceinline__ long long share_holding(long long T, long long t,
+                                                            long long NS, int skew) {
+  long long j = (t * NS) / T;              // exact without skew; off by at most one with it
+  while (j > 0 && share_cut(T, j, NS, skew) > t) --j;
+  while (j + 1 < NS && share_cut(T, j + 1, NS, skew) <= t) ++j;
+  return j;
+}
 
 __device__ __forceinline__ size_t rec_acc_index(int slice, long long rec, int h, int G,
                                                 long long R) {
@@ -754,10 +780,20 @@ template <int D, class DT, int W>
 __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) Phase1Lds<D, W> sm;
   int wg = blockIdx.x;
-  const int unit = wg % a.units;
-  wg /= a.units;
-  const int s = wg % a.num_seqs;
-  const int part = wg / a.num_seqs;
+  int unit, s, part;
+  if (a.xcd_skew > 0) {
+    // partition fastest, so the two partitions of a pair run on XCDs of opposite
+    // parity
+    part = wg % a.max_parts;
+    wg /= a.max_parts;
+    unit = wg % a.units;
+    s = wg / a.units;
+  } else {
+    unit = wg % a.units;
+    wg /= a.units;
+    s = wg % a.num_seqs;
+    part = wg / a.num_seqs;
+  }
   const int L = clamp_len(a, s);
   const bool single = L <= a.single_pass_max_len;
   int t_begin, t_end;
@@ -766,10 +802,22 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_kernel(DecodeArgs a) 
     t_begin = 0;
     t_end = L > 0 ? L : 0;
   } else {
-    const int np = (L + a.partition_size - 1) / a.partition_size;
+    const int P = a.partition_size;
+    const int np = (L + P - 1) / P;
     if (part >= np) return;
-    t_begin = part * a.partition_size;
-    t_end = min(L, t_begin + a.partition_size);
+    t_begin = part * P;
+    t_end = min(L, t_begin + P);
+    if (a.xcd_skew > 0 && (part | 1) < np) {
+      // partitions 2i and 2i+1 split [2iP, 2iP + 2P) at a 16-token cut that gives
+      // the member with the even block index (even XCD) the larger part
+      const int base = (part & ~1) * P;
+      const int big = min(2 * P, (P + P / 1000 * a.xcd_skew + P % 1000 * a.xcd_skew / 1000 +
+                                  kTile - 1) / kTile * kTile);
+      const bool first_big = ((blockIdx.x - (part & 1)) & 1) == 0;
+      const int cut = base + (first_big ? big : 2 * P - big);
+      t_begin = (part & 1) ? min(L, cut) : base;
+      t_end = (part & 1) ? min(L, base + 2 * P) : min(L, cut);
+    }
   }
   const long long seg = (long long)s * a.units + unit;
   const long long rec = seg * a.max_parts + part;
@@ -784,10 +832,14 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_kernel(DecodeArgs a) 
 }
 
 // Balanced mode.  Sequence s has n(s) = ceil(L_s/16) tiles per KV head; laid end
-// to end they make T tiles, cut into NS = num_wg/Hkv equal shares.  Workgroup w
-// takes share j = w / Hkv of KV head kvh = w % Hkv, so the Hkv workgroups of a
-// share run side by side and read the Hkv contiguous chunks of the same pages.
-// Each workgroup rebuilds the per-sequence prefix of tiles in LDS from seq_lens
+// to end they make T tiles, cut into NS = num_wg/Hkv shares.  Workgroup w takes
+// share j = w / Hkv of KV head kvh = w % Hkv, so the Hkv workgroups of a share
+// run side by side and read the Hkv contiguous chunks of the same pages; with
+// XCD-paired shares (xcd_skew > 0, NS even) workgroup w takes share
+// j = 2*(w / (2*Hkv)) + w % 2 of KV head (w / 2) % Hkv instead, so the two shares
+// of a pair run on XCDs of opposite parity and the even one is the larger.  Its
+// partial records are indexed by r = j*Hkv + kvh either way.  Each workgroup
+// rebuilds the per-sequence prefix of tiles in LDS from seq_lens
 // (S <= kMaxBalancedSeqs), then walks its share.
 template <int D, class DT, int W>
 __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(DecodeArgs a) {
@@ -804,7 +856,10 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(Decod
   const int S = a.num_seqs, Hkv = a.num_kv_heads;
   const int w = blockIdx.x;
   const int NS = a.num_wg / Hkv;
-  const int j = w / Hkv, kvh = w % Hkv;
+  const int skew = a.xcd_skew;
+  const int j = skew > 0 ? 2 * (w / (2 * Hkv)) + (w & 1) : w / Hkv;
+  const int kvh = skew > 0 ? (w >> 1) % Hkv : w % Hkv;
+  const int r = j * Hkv + kvh;      // record slot pair and job of this share
 
   // ---- inclusive scan of tiles per sequence: thread tid owns sequences tid*PER ..
   int local[PER];
@@ -841,7 +896,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(Decod
 
   // everything below is the same for all lanes: keep it in scalar registers
   const int T = uniform(pre[S]);
-  const long long lo = (long long)T * j / NS, hi = (long long)T * (j + 1) / NS;
+  const long long lo = share_cut(T, j, NS, skew), hi = share_cut(T, j + 1, NS, skew);
 
   // sequences of length <= 0 get zero rows; spread over the workgroups
   for (int s = w; s < S; s += a.num_wg) {
@@ -852,8 +907,8 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(Decod
     }
   }
 
-  // share holding tile t: largest j with T*j/NS <= t
-  auto share_of = [&](long long t) { return ((t + 1) * NS - 1) / T; };
+  // share holding tile t
+  auto share_of = [&](long long t) { return share_holding(T, t, NS, skew); };
   // the records of sequence s's partials: slot 1 of the share that begins it, then
   // slot 0 of each following share up to the one holding its last tile
   auto seg_merge = [&](int s) {
@@ -878,9 +933,9 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(Decod
     // neighbouring shares split: leave the identity (-inf, 0) in slot 0
     for (int h = tid; h < a.group; h += NT) {
       if (a.tickets != nullptr)
-        store_dev(a.ws_ml + 2LL * w * a.group + h, make_float2(kNegInf, 0.f));
+        store_dev(a.ws_ml + 2LL * r * a.group + h, make_float2(kNegInf, 0.f));
       else
-        a.ws_ml[2LL * w * a.group + h] = make_float2(kNegInf, 0.f);
+        a.ws_ml[2LL * r * a.group + h] = make_float2(kNegInf, 0.f);
     }
     if (a.tickets != nullptr && lo > 0 && lo < T) {
       // inside sequence s iff tiles lo - 1 and lo both belong to it; the identity
@@ -898,12 +953,11 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(Decod
       const int ta = x - seg0;
       const int tb = min(x_end, seg1) - seg0;
       const bool final = ta == 0 && tb == n;
-      const long long rec = 2LL * w + (ta > 0 ? 0 : 1);
+      const long long rec = 2LL * r + (ta > 0 ? 0 : 1);
       if (ta == 0 && !final) {
         // this share starts a sequence that later shares continue: it owns the merge
-        const long long last = ((long long)seg1 * NS - 1) / T;   // share holding tile seg1-1
         job_q = s * Hkv + kvh;
-        job_n = static_cast<int>(last - j + 1);
+        job_n = static_cast<int>(share_of(seg1 - 1) - j + 1);
       }
       // the piece ends at its last tile, or at the sequence's last token
       const int t_end = tb == n ? kTile * (n - 1) + uniform(last_len[s]) : kTile * tb;
@@ -913,7 +967,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(Decod
       do { ++s; } while (s < S && uniform(pre[s + 1]) == uniform(pre[s]) && x < x_end);
     }
   }
-  if (tid == 0) a.jobs[w] = make_int2(job_q, job_n);
+  if (tid == 0) a.jobs[r] = make_int2(job_q, job_n);
 }
 
 // ---------------------------------------------------------------------------

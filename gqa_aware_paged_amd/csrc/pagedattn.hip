@@ -35,6 +35,11 @@ constexpr int kDefaultCUs = 256;            // MI355X
 constexpr float kLog2e = 1.4426950408889634f;
 
 constexpr int kMinTilesPerWG = 4;         // balanced mode: at least one tile per wave
+// XCD-paired shares: permille of a pair's mean the member on the even XCD takes
+// in addition.  Measured on 4 x 102400 tokens with fixed partitions: per-XCD
+// mean workgroup times even out at 80 (odd XCDs ~8-10% slower with equal
+// shares), 258.4 -> 252.2 us/step.
+constexpr int kDefaultXcdSkew = 80;
 constexpr int kBalancedSlices = 8;        // balanced phase 2: 16-wide slices per workgroup
 
 // 16-wide head_dim slices one balanced phase-2 workgroup merges
@@ -49,6 +54,7 @@ struct Plan {
   int group = 0;         // query heads per workgroup
   int units = 0;         // head units per sequence (num_kv_heads, or num_heads)
   int num_wg = 0;        // phase-1 workgroups, balanced mode
+  int xcd_skew = 0;      // XCD-paired shares (permille), 0 = equal shares
   long long records = 0; // partial records in the workspace
   long long grid1 = 0, grid2 = 0;
   bool fused = false;    // partials merged in phase 1 (ticket counters), no phase 2
@@ -117,11 +123,20 @@ int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int 
   const bool forced_tier = opt && opt->single_pass_max_len >= 0;
   // a host-side total equal to num_seqs * max_seq_len means every sequence is at
   // the bound: fixed partitions of one workgroup per CU are then exactly balanced
-  // and need no device-side prefix of seq_lens
+  // and need no device-side prefix of seq_lens, as long as there are no more
+  // segments than workgroup slots (256 x 16384 tokens, 1024 segments: fixed
+  // partitions of whole sequences 2617 us, the balanced split 2559 us)
   const long long hint = opt ? opt->total_tokens_hint : 0;
-  const bool uniform = hint > 0 && hint == static_cast<long long>(S) * pl.max_seq_len;
+  const long long slots_all = static_cast<long long>(cus) * workgroups_per_cu(D, bs);
+  const bool uniform = hint > 0 && hint == static_cast<long long>(S) * pl.max_seq_len &&
+                       static_cast<long long>(S) * pl.units <= slots_all;
   pl.balanced = P_req == 0 && !forced_tier && !uniform && !per_qhead &&
                 S <= pa::kMaxBalancedSeqs;
+  // XCD-paired shares apply to automatic splits only: explicit partition sizes
+  // (the pages' grid) and the per-query-head ablation keep equal partitions
+  int skew = opt ? opt->xcd_skew : 0;
+  skew = skew == 0 ? kDefaultXcdSkew : (skew < 0 ? 0 : (skew > 500 ? 500 : skew));
+  if (P_req != 0 || per_qhead) skew = 0;
   if (pl.balanced) {
     // shares x KV heads: workgroups_per_cu resident workgroups per CU (measured on
     // the batch and long workloads as for fixed partitions: one per CU at head_dim
@@ -134,6 +149,7 @@ int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int 
     if (ns > ns_max) ns = ns_max;
     if (ns < 1) ns = 1;
     pl.num_wg = static_cast<int>(ns * Hkv);
+    pl.xcd_skew = ns % 2 == 0 ? skew : 0;     // shares pair up across XCD parities
     pl.records = 2LL * pl.num_wg;
     pl.grid1 = pl.num_wg;
     pl.grid2 = static_cast<long long>(pl.num_wg) * (D / 16 / balanced_slices(D));
@@ -146,6 +162,7 @@ int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int 
     // a sequence that fits in one partition is served in one pass
     pl.T1 = forced_tier ? opt->single_pass_max_len : pl.P;
     if (pl.max_seq_len > pl.T1) pl.max_parts = (pl.max_seq_len + pl.P - 1) / pl.P;
+    pl.xcd_skew = pl.max_parts >= 2 ? skew : 0;
     const long long parts = pl.max_parts > 0 ? pl.max_parts : 1;
     pl.grid1 = static_cast<long long>(S) * pl.units * parts;
     pl.grid2 = pl.max_parts > 0 ? static_cast<long long>(S) * pl.units * (D / 16) : 0;
@@ -295,6 +312,7 @@ PA_API int paged_attn_plan(const int32_t* seq_lens_host, int num_seqs, int num_h
   info->lds_bytes_phase1 = kWaves * 2 * pa::kTile * head_dim * 2;
   info->balanced = pl.balanced ? 1 : 0;
   info->fused = pl.fused ? 1 : 0;
+  info->xcd_skew = pl.xcd_skew;
   if (seq_lens_host) {
     if (pl.balanced) {
       // host mirror of the device split: sequence s covers tiles [pre_s, pre_s + n)
@@ -305,18 +323,20 @@ PA_API int paged_attn_plan(const int32_t* seq_lens_host, int num_seqs, int num_h
         T += L > 0 ? (L + 15) / 16 : 0;
       }
       const long long NS = pl.num_wg / num_kv_heads;
+      const int sk = pl.xcd_skew;
       long long start = 0;
       for (int s = 0; s < num_seqs; ++s) {
         const int L = seq_lens_host[s] < pl.max_seq_len ? seq_lens_host[s] : pl.max_seq_len;
         const long long n = L > 0 ? (L + 15) / 16 : 0;
-        if (n > 0 && ((start + 1) * NS - 1) / T != ((start + n) * NS - 1) / T)
+        if (n > 0 && pa::share_holding(T, start, NS, sk) != pa::share_holding(T, start + n - 1, NS, sk))
           info->partitioned_seqs++;
         else
           info->single_pass_seqs++;
         start += n;
       }
       for (long long j = 0; j < NS; ++j)
-        if (T * j / NS < T * (j + 1) / NS) info->active_workgroups += num_kv_heads;
+        if (pa::share_cut(T, j, NS, sk) < pa::share_cut(T, j + 1, NS, sk))
+          info->active_workgroups += num_kv_heads;
     } else {
       for (int s = 0; s < num_seqs; ++s) {
         const int L = seq_lens_host[s] < pl.max_seq_len ? seq_lens_host[s] : pl.max_seq_len;
@@ -373,6 +393,7 @@ PA_API int paged_attn_decode_ex(void* out, const void* q, const void* key_cache,
   args.jobs = pl.balanced && pl.ws_bytes ? reinterpret_cast<int2*>(ws + pl.ws_jobs_off) : nullptr;
   args.records = pl.records;
   args.num_wg = pl.num_wg;
+  args.xcd_skew = pl.xcd_skew;
   args.num_seqs = num_seqs;
   args.num_heads = num_heads;
   args.num_kv_heads = num_kv_heads;

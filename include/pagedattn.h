@@ -102,8 +102,9 @@ typedef struct pa_options {
     /* Sum of seq_lens if the caller knows it on the host (0 = unknown).  Only
      * used when partition_size is 0: a total of num_seqs * max_seq_len (every
      * sequence at the bound) selects fixed partitions of one workgroup per CU
-     * instead of the device-side balanced split; with a forced tier it sizes the
-     * automatic partitions. */
+     * instead of the device-side balanced split, when num_seqs * num_kv_heads
+     * does not exceed the workgroup slots (256 CUs x w, w as below); with a
+     * forced tier it sizes the automatic partitions. */
     long long total_tokens_hint;
     /* Ablation only: 1 launches one workgroup per query head instead of one per
      * KV head (the GQA-unaware grid; each KV page is read once per query head).
@@ -119,7 +120,15 @@ typedef struct pa_options {
      * runs) when num_seqs * num_kv_heads (num_heads with per_query_head)
      * exceeds PA_WORKSPACE_TICKET_BYTES / 4. */
     int fused_combine;
-    int reserved[2];
+    /* Automatic splits only (partition_size 0): the hardware hands out
+     * workgroup i to XCD i mod 8, and the workgroups of the odd XCDs of MI355X
+     * stream K/V ~8-10% slower than those of the even ones, so shares are paired
+     * across XCD parities and the even member takes this many permille of the
+     * pair's mean more (the odd one as many less).  0 = default (80); negative =
+     * equal shares; at most 500.  Share boundaries stay fixed for given sizes, so
+     * results do not depend on timing. */
+    int xcd_skew;
+    int reserved;
     /* If non-NULL, hipEventRecord(phase1_begin/phase1_end, stream) is issued
      * immediately before/after the phase-1 kernel (instrumentation only). */
     hipEvent_t phase1_begin;
@@ -142,6 +151,7 @@ typedef struct pa_plan_info {
     int lds_bytes_phase1;      /* LDS of the phase-1 tile slots             */
     int balanced;              /* 1: length-balanced split (partition_size 0) */
     int fused;                 /* 1: partials merged in phase 1, no phase-2 launch */
+    int xcd_skew;              /* XCD-paired shares in use (permille), 0 = equal */
 } pa_plan_info;
 
 /*
@@ -185,7 +195,8 @@ size_t paged_attn_workspace_size_ex(int num_seqs, int num_heads, int num_kv_head
  *                       step's tiles cut on the device into equal shares, one
  *                       workgroup per share and KV head, w per CU as below) for up
  *                       to 1024 sequences; with equal lengths declared through
- *                       pa_options.total_tokens_hint, more sequences, or a forced
+ *                       pa_options.total_tokens_hint (and no more segments than
+ *                       workgroup slots), more sequences, or a forced
  *                       tier, it is fixed partitions of ceil(num_seqs *
  *                       max_seq_len * num_kv_heads / (256 * w)) tokens rounded up
  *                       to 16, at least 64 and at most max_seq_len, where w (the

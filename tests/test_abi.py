@@ -159,10 +159,14 @@ def test_balanced_split_plan(lib):
     assert info["phase2_workgroups"] == 256 * 2
     assert pa.plan([L] * 4, 24, 4, 128, 16, L // 16, L, 0)["phase1_workgroups"] == 512
     assert pa.plan([L] * 4, 24, 4, 256, 8, L // 8, L, 0)["phase1_workgroups"] == 512
-    # 1024 segments of 1024 tiles over 256 workgroups: shares end on segment ends
-    info = pa.plan([16384] * 256, 24, 4, 256, 32, 512, 16384, 0)
-    assert info["phase1_workgroups"] == 256
+    # 1024 segments of 1024 tiles over 256 workgroups: equal shares end on segment ends
+    info = pa.plan([16384] * 256, 24, 4, 256, 32, 512, 16384, 0, xcd_skew=-1)
+    assert info["phase1_workgroups"] == 256 and info["xcd_skew"] == 0
     assert info["single_pass_seqs"] == 256 and info["partitioned_seqs"] == 0
+    # XCD-paired shares (4.32 and 3.68 sequences per pair of 8): one cut per pair
+    info = pa.plan([16384] * 256, 24, 4, 256, 32, 512, 16384, 0)
+    assert info["phase1_workgroups"] == 256 and info["xcd_skew"] == 80
+    assert info["single_pass_seqs"] == 224 and info["partitioned_seqs"] == 32
     # short: one workgroup per 4 tiles (one per wave) of the length bound
     info = pa.plan([100] * 8, 24, 4, 256, 16, 8, 100, 0)
     assert info["phase1_workgroups"] == 4 * ((8 * 7 + 3) // 4)   # shares x KV heads
@@ -195,6 +199,9 @@ def test_automatic_partition_size_for_256_cus(lib):
     info = pa.plan([16384] * 1100, 24, 4, 256, 32, 512, 16384, 0)   # too many for the split
     assert info["balanced"] == 0 and info["partition_size"] == 16384
     assert info["partitioned_seqs"] == 0 and info["workspace_bytes"] == 0
+    # equal lengths but more segments (256 x 4) than workgroup slots: balanced split
+    info = pa.plan([16384] * 256, 24, 4, 256, 32, 512, 16384, 0, total_tokens_hint=256 * 16384)
+    assert info["balanced"] == 1
     # a host-side total shrinks the partitions of an unequal batch
     lens = [64] * 1100 + [65536] * 4
     a = pa.plan(lens, 24, 4, 256, 16, 4096, 65536, 0)
@@ -292,3 +299,28 @@ def test_prefill_validation_errors_before_any_launch(lib):
     assert prefill_call(lib, out=ctypes.c_void_p(0x10004)) == 7
     assert prefill_call(lib, S=0) == 0                      # nothing to do
     assert prefill_call(lib, mq=0) == 0
+
+
+def test_xcd_paired_shares_plan(lib):
+    """Automatic splits pair their shares across XCD parities (default 80 permille);
+    explicit partition sizes and the per-query-head ablation keep equal ones."""
+    L = 102400
+    hinted = pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0, total_tokens_hint=4 * L)
+    assert hinted["balanced"] == 0 and hinted["max_partitions"] == 16
+    assert hinted["xcd_skew"] == 80
+    assert pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0, total_tokens_hint=4 * L,
+                   xcd_skew=30)["xcd_skew"] == 30
+    assert pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0, total_tokens_hint=4 * L,
+                   xcd_skew=-1)["xcd_skew"] == 0
+    assert pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0, total_tokens_hint=4 * L,
+                   xcd_skew=900)["xcd_skew"] == 500
+    assert pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 512)["xcd_skew"] == 0
+    assert pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0, total_tokens_hint=4 * L,
+                   per_query_head=True)["xcd_skew"] == 0
+    assert pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0)["xcd_skew"] == 80
+    # an odd number of shares per KV head cannot pair up
+    odd = pa.plan([40] * 3, 24, 4, 256, 16, 3, 40, 0)
+    assert odd["balanced"] == 1 and odd["phase1_workgroups"] == 4 * 3 and odd["xcd_skew"] == 0
+    # a single partition per sequence has nothing to pair
+    assert pa.plan([5000] * 2, 24, 4, 256, 16, 313, 5000, 0, total_tokens_hint=10000,
+                   single_pass_max_len=1 << 20)["xcd_skew"] == 0

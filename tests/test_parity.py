@@ -318,3 +318,39 @@ def test_workspace_reuse_and_stream():
             out = dec(w.q, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, w.scale)
     torch.cuda.current_stream().wait_stream(side)
     assert_close(gpu_out(out), ref, "decoder")
+
+
+# ---------------------------------------------------------------------------
+# XCD-paired shares (automatic splits)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("skew", [-1, 30, 80, 500])
+def test_xcd_skew_balanced(skew):
+    """Balanced split with paired shares of unequal size: a length mix with zero
+    lengths; the result matches the oracle for any skew, and a repeat is bitwise
+    identical."""
+    say(f"case xcd skew balanced {skew}")
+    w = make([5000, 0, 64, 12000, 700, 1, 9000, 33, 20000, 3], seed=80)
+    info = pa.plan(list(w.seq_lens_host), 24, 4, 256, 16, w.max_blocks_per_seq, w.max_seq_len,
+                   0, xcd_skew=skew)
+    assert info["balanced"] == 1 and info["xcd_skew"] == max(skew, 0)
+    out = run(w, P=0, xcd_skew=skew)
+    assert_close(gpu_out(out), oracle_full(w), f"xcd/balanced/{skew}")
+    assert torch.equal(out, run(w, P=0, xcd_skew=skew))
+
+
+@pytest.mark.parametrize("lens", [[9000] * 3, [4200] * 2, [16 * 33] * 5])
+@pytest.mark.parametrize("skew", [80, 500])
+def test_xcd_skew_fixed(lens, skew):
+    """Automatic fixed partitions (equal lengths declared) with paired partitions:
+    an odd partition count leaves the last one unpaired, and a last pair past the
+    length leaves an empty partial."""
+    say(f"case xcd skew fixed lens={lens[0]}x{len(lens)} skew={skew}")
+    w = make(lens, seed=81)
+    hint = int(sum(lens))
+    info = pa.plan(list(w.seq_lens_host), 24, 4, 256, 16, w.max_blocks_per_seq, w.max_seq_len,
+                   0, total_tokens_hint=hint, xcd_skew=skew)
+    assert info["balanced"] == 0 and info["max_partitions"] >= 2
+    assert info["xcd_skew"] == skew
+    out = run(w, P=0, total_tokens_hint=hint, xcd_skew=skew)
+    assert_close(gpu_out(out), oracle_full(w), f"xcd/fixed/{lens[0]}/{skew}")
