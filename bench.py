@@ -89,7 +89,8 @@ def default_command(args) -> bool:
     return (args.workload == "long" and args.partition_size == 0 and not args.p512
             and args.single_pass_max_len is None and not args.per_query_head
             and not args.fused and not args.no_hint and args.num_cus == 0
-            and args.head_dim == 256 and args.block_size == 16 and args.xcd_skew == 0)
+            and args.head_dim == 256 and args.block_size == 16 and args.xcd_skew == 0
+            and args.piece_cost == 0)
 
 
 def cpu_baseline(w, nseqs: int):
@@ -218,6 +219,9 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=4,
                     help="sequences of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--piece-cost", type=int, default=0,
+                    help="balanced split: tiles a piece start counts as (0 = library default, "
+                         "-1 = none)")
     ap.add_argument("--xcd-skew", type=int, default=0,
                     help="automatic splits: permille the even-XCD share of a pair takes "
                          "above the mean (0 = library default, -1 = equal shares)")
@@ -262,7 +266,7 @@ def main():
                           partition_size=P, single_pass_max_len=args.single_pass_max_len,
                           num_cus=args.num_cus, total_tokens_hint=total,
                           per_query_head=args.per_query_head, fused_combine=args.fused,
-                          xcd_skew=args.xcd_skew)
+                          xcd_skew=args.xcd_skew, piece_cost=args.piece_cost)
 
     P = args.partition_size
     # the caller knows its sequence lengths on the host: pass their sum
@@ -272,7 +276,8 @@ def main():
                    w.block_size, w.max_blocks_per_seq, w.max_seq_len, P,
                    single_pass_max_len=args.single_pass_max_len, num_cus=args.num_cus,
                    total_tokens_hint=total, per_query_head=args.per_query_head,
-                   fused_combine=args.fused, xcd_skew=args.xcd_skew)
+                   fused_combine=args.fused, xcd_skew=args.xcd_skew,
+                   piece_cost=args.piece_cost)
     log(f"plan: {info}")
 
     if args.copy_probe_mib > 0:
@@ -391,6 +396,7 @@ def main():
                    "single_pass_max_len": info["single_pass_max_len"],
                    "split": "balanced" if info["balanced"] else "fixed partitions",
                    "xcd_skew_permille": info["xcd_skew"],
+                   "piece_cost_tiles": info["piece_cost"] if info["balanced"] else None,
                    "grid": "per query head (ablation)" if args.per_query_head else "per KV head",
                    "combine": "fused in phase 1" if info["fused"] else
                    ("phase-2 kernel" if info["phase2_workgroups"] else "none (one pass)"),

@@ -27,7 +27,7 @@ class Options(ctypes.Structure):
     _fields_ = [("single_pass_max_len", ctypes.c_int), ("num_cus", ctypes.c_int),
                 ("total_tokens_hint", ctypes.c_longlong), ("per_query_head", ctypes.c_int),
                 ("fused_combine", ctypes.c_int), ("xcd_skew", ctypes.c_int),
-                ("reserved", ctypes.c_int),
+                ("piece_cost", ctypes.c_int),
                 ("phase1_begin", ctypes.c_void_p), ("phase1_end", ctypes.c_void_p)]
 
 
@@ -40,7 +40,7 @@ class PlanInfo(ctypes.Structure):
                 ("partitioned_seqs", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t),
                 ("threads_per_workgroup", ctypes.c_int), ("lds_bytes_phase1", ctypes.c_int),
                 ("balanced", ctypes.c_int), ("fused", ctypes.c_int),
-                ("xcd_skew", ctypes.c_int)]
+                ("xcd_skew", ctypes.c_int), ("piece_cost", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -97,9 +97,10 @@ def _check(status: int):
 def _opts(single_pass_max_len: Optional[int], num_cus: int = 0,
           events: Optional[Tuple[int, int]] = None, total_tokens_hint: int = 0,
           per_query_head: bool = False, fused_combine: bool = False,
-          xcd_skew: int = 0) -> Options:
+          xcd_skew: int = 0, piece_cost: int = 0) -> Options:
     o = Options()
     o.xcd_skew = int(xcd_skew)
+    o.piece_cost = int(piece_cost)
     o.per_query_head = 1 if per_query_head else 0
     o.fused_combine = 1 if fused_combine else 0
     o.single_pass_max_len = -1 if single_pass_max_len is None else int(single_pass_max_len)
@@ -119,7 +120,7 @@ def plan(seq_lens_host, num_heads: int, num_kv_heads: int, head_dim: int, block_
          dtype: int = PA_F16, single_pass_max_len: Optional[int] = None,
          num_seqs: Optional[int] = None, num_cus: int = 0, total_tokens_hint: int = 0,
          per_query_head: bool = False, fused_combine: bool = False,
-         xcd_skew: int = 0) -> dict:
+         xcd_skew: int = 0, piece_cost: int = 0) -> dict:
     """Host-only plan (no GPU needed).  seq_lens_host: sequence of ints or None."""
     arr = None
     if seq_lens_host is not None:
@@ -128,7 +129,8 @@ def plan(seq_lens_host, num_heads: int, num_kv_heads: int, head_dim: int, block_
         num_seqs = n
     info = PlanInfo()
     o = _opts(single_pass_max_len, num_cus, total_tokens_hint=total_tokens_hint,
-              per_query_head=per_query_head, fused_combine=fused_combine, xcd_skew=xcd_skew)
+              per_query_head=per_query_head, fused_combine=fused_combine, xcd_skew=xcd_skew,
+              piece_cost=piece_cost)
     _check(lib().paged_attn_plan(arr, int(num_seqs or 0), num_heads, num_kv_heads, head_dim,
                                  block_size, max_blocks_per_seq, max_seq_len, partition_size,
                                  dtype, ctypes.byref(o), ctypes.byref(info)))
@@ -173,7 +175,8 @@ class Decoder:
                  max_seq_len: int = 0, partition_size: int = 0,
                  single_pass_max_len: Optional[int] = None, total_tokens_hint: int = 0,
                  num_cus: int = 0, per_query_head: bool = False,
-                 fused_combine: bool = False, xcd_skew: int = 0, device="cuda"):
+                 fused_combine: bool = False, xcd_skew: int = 0, piece_cost: int = 0,
+                 device="cuda"):
         self.shape = (num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                       max_blocks_per_seq)
         self.dtype = dtype
@@ -181,7 +184,7 @@ class Decoder:
         self.partition_size = int(partition_size)
         self.opts = _opts(single_pass_max_len, num_cus, total_tokens_hint=total_tokens_hint,
                           per_query_head=per_query_head, fused_combine=fused_combine,
-                          xcd_skew=xcd_skew)
+                          xcd_skew=xcd_skew, piece_cost=piece_cost)
         nbytes = workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                                 max_blocks_per_seq, max_seq_len, partition_size,
                                 single_pass_max_len, total_tokens_hint, num_cus,
@@ -232,7 +235,7 @@ def decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
            workspace: Optional[torch.Tensor] = None, single_pass_max_len: Optional[int] = None,
            events: Optional[Tuple[int, int]] = None, total_tokens_hint: int = 0,
            per_query_head: bool = False, fused_combine: bool = False,
-           xcd_skew: int = 0) -> torch.Tensor:
+           xcd_skew: int = 0, piece_cost: int = 0) -> torch.Tensor:
     """One decode step: out[s,h] = softmax(scale q K^T) V over the paged caches.
 
     fused_combine: merge partitions inside phase 1; a workspace passed in must then
@@ -250,7 +253,8 @@ def decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
     if out is None:
         out = torch.empty_like(q)
     o = _opts(single_pass_max_len, events=events, total_tokens_hint=total_tokens_hint,
-              per_query_head=per_query_head, fused_combine=fused_combine, xcd_skew=xcd_skew)
+              per_query_head=per_query_head, fused_combine=fused_combine, xcd_skew=xcd_skew,
+              piece_cost=piece_cost)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(lib().paged_attn_decode_ex(
         _ptr(out), _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),

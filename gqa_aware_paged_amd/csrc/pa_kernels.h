@@ -151,7 +151,8 @@ struct DecodeArgs {
   int max_parts;            // grid mode
   int num_wg;               // balanced mode: workgroups of phase 1
   int xcd_skew;             // XCD-paired shares: permille the even-XCD member of a pair
-                            // takes above the mean (0: equal shares), see xcd_cut
+                            // takes above the mean (0: equal shares), see share_cut
+  int piece_cost;           // balanced mode: tiles a piece's start is worth in the cut
   float scale_log2;         // scale * log2(e)
 };
 
@@ -840,13 +841,17 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_kernel(DecodeArgs a) 
 // of a pair run on XCDs of opposite parity and the even one is the larger.  Its
 // partial records are indexed by r = j*Hkv + kvh either way.  Each workgroup
 // rebuilds the per-sequence prefix of tiles in LDS from seq_lens
-// (S <= kMaxBalancedSeqs), then walks its share.
+// (S <= kMaxBalancedSeqs), then walks its share.  Starting a piece costs about
+// as much as streaming piece_cost tiles (its Q, block-table and first K/V round
+// trips, the wave merge and the record), so every sequence with tokens counts
+// piece_cost virtual tiles before its real ones, and the shares are cut in
+// these virtual tiles: a share that starts more pieces gets fewer real tiles.
 template <int D, class DT, int W>
 __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(DecodeArgs a) {
   constexpr int NT = W * 64;
   constexpr int PER = kMaxBalancedSeqs / NT;
   __shared__ __attribute__((aligned(16))) Phase1Lds<D, W> sm;
-  __shared__ int pre[kMaxBalancedSeqs + 1];     // pre[s] = tiles of sequences < s (one KV head)
+  __shared__ int pre[kMaxBalancedSeqs + 1];     // pre[s] = virtual tiles of sequences < s
   __shared__ unsigned char last_len[kMaxBalancedSeqs];   // tokens in a sequence's last tile
   __shared__ int wave_tot[W];
 
@@ -860,6 +865,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(Decod
   const int j = skew > 0 ? 2 * (w / (2 * Hkv)) + (w & 1) : w / Hkv;
   const int kvh = skew > 0 ? (w >> 1) % Hkv : w % Hkv;
   const int r = j * Hkv + kvh;      // record slot pair and job of this share
+  const int c = a.piece_cost;       // virtual tiles ahead of each sequence with tokens
 
   // ---- inclusive scan of tiles per sequence: thread tid owns sequences tid*PER ..
   int local[PER];
@@ -872,6 +878,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(Decod
       const int L = clamp_len(a, s);
       n = L > 0 ? (L + kTile - 1) / kTile : 0;
       last_len[s] = static_cast<unsigned char>(L > 0 ? L - kTile * (n - 1) : 0);
+      if (n > 0) n += c;
     }
     tsum += n;
     local[i] = tsum;
@@ -909,10 +916,10 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(Decod
 
   // share holding tile t
   auto share_of = [&](long long t) { return share_holding(T, t, NS, skew); };
-  // the records of sequence s's partials: slot 1 of the share that begins it, then
-  // slot 0 of each following share up to the one holding its last tile
+  // the records of sequence s's partials: slot 1 of the share that holds its first
+  // real tile, then slot 0 of each following share up to the one holding its last
   auto seg_merge = [&](int s) {
-    const long long j0 = share_of(uniform(pre[s]));
+    const long long j0 = share_of(uniform(pre[s]) + c);
     const long long j1 = share_of(uniform(pre[s + 1]) - 1);
     return SegMerge{s * Hkv + kvh, static_cast<int>(j1 - j0 + 1), 2 * (j0 * Hkv + kvh),
                     2LL * Hkv, 1};
@@ -938,31 +945,35 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(Decod
         a.ws_ml[2LL * r * a.group + h] = make_float2(kNegInf, 0.f);
     }
     if (a.tickets != nullptr && lo > 0 && lo < T) {
-      // inside sequence s iff tiles lo - 1 and lo both belong to it; the identity
-      // then counts among its partials
+      // inside sequence s iff tiles lo - 1 and lo are both real tiles of it; the
+      // identity then counts among its partials
       const int s = seq_of(lo);
-      if (uniform(pre[s]) < lo) finish_partial<D, DT, W>(a, sm, s, kvh, seg_merge(s));
+      if (uniform(pre[s]) + c < lo) finish_partial<D, DT, W>(a, sm, s, kvh, seg_merge(s));
     }
   } else {
     int s = seq_of(lo);
     int x = static_cast<int>(lo);
     const int x_end = static_cast<int>(hi);
     while (x < x_end) {
-      const int seg0 = uniform(pre[s]), seg1 = uniform(pre[s + 1]);
+      // real tiles of s: virtual [seg0, seg1); the share's part of them, if any
+      const int seg0 = uniform(pre[s]) + c, seg1 = uniform(pre[s + 1]);
       const int n = seg1 - seg0;
-      const int ta = x - seg0;
-      const int tb = min(x_end, seg1) - seg0;
-      const bool final = ta == 0 && tb == n;
-      const long long rec = 2LL * r + (ta > 0 ? 0 : 1);
-      if (ta == 0 && !final) {
-        // this share starts a sequence that later shares continue: it owns the merge
-        job_q = s * Hkv + kvh;
-        job_n = static_cast<int>(share_of(seg1 - 1) - j + 1);
+      const int xs = max(x, seg0), xe = min(x_end, seg1);
+      if (xs < xe) {
+        const int ta = xs - seg0;
+        const int tb = xe - seg0;
+        const bool final = ta == 0 && tb == n;
+        const long long rec = 2LL * r + (ta > 0 ? 0 : 1);
+        if (ta == 0 && !final) {
+          // this share starts a sequence that later shares continue: it owns the merge
+          job_q = s * Hkv + kvh;
+          job_n = static_cast<int>(share_of(seg1 - 1) - j + 1);
+        }
+        // the piece ends at its last tile, or at the sequence's last token
+        const int t_end = tb == n ? kTile * (n - 1) + uniform(last_len[s]) : kTile * tb;
+        run_piece<D, DT, W>(a, sm, s, kvh, kTile * ta, t_end, final, rec,
+                            final ? SegMerge{-1, 0, 0, 0, 0} : seg_merge(s));
       }
-      // the piece ends at its last tile, or at the sequence's last token
-      const int t_end = tb == n ? kTile * (n - 1) + uniform(last_len[s]) : kTile * tb;
-      run_piece<D, DT, W>(a, sm, s, kvh, kTile * ta, t_end, final, rec,
-                          final ? SegMerge{-1, 0, 0, 0, 0} : seg_merge(s));
       x = min(seg1, x_end);
       do { ++s; } while (s < S && uniform(pre[s + 1]) == uniform(pre[s]) && x < x_end);
     }

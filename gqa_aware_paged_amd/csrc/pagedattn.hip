@@ -40,6 +40,12 @@ constexpr int kMinTilesPerWG = 4;         // balanced mode: at least one tile pe
 // mean workgroup times even out at 80 (odd XCDs ~8-10% slower with equal
 // shares), 258.4 -> 252.2 us/step.
 constexpr int kDefaultXcdSkew = 80;
+// Balanced mode: tiles of streaming a piece's start costs (head_dim 256, one
+// workgroup per CU).  Measured on 32 x U[512, 8192] with equal shares: a share
+// holding two pieces ran 4.8 us (about 8 tiles) longer than one holding one.
+// Scaled to other head sizes (a tile carries head_dim/256 of the bytes) and
+// halved with two workgroups per CU (each streams at half the rate).
+constexpr int kPieceCostTiles = 8;
 constexpr int kBalancedSlices = 8;        // balanced phase 2: 16-wide slices per workgroup
 
 // 16-wide head_dim slices one balanced phase-2 workgroup merges
@@ -55,6 +61,7 @@ struct Plan {
   int units = 0;         // head units per sequence (num_kv_heads, or num_heads)
   int num_wg = 0;        // phase-1 workgroups, balanced mode
   int xcd_skew = 0;      // XCD-paired shares (permille), 0 = equal shares
+  int piece_cost = 0;    // balanced mode: virtual tiles per sequence start
   long long records = 0; // partial records in the workspace
   long long grid1 = 0, grid2 = 0;
   bool fused = false;    // partials merged in phase 1 (ticket counters), no phase 2
@@ -150,6 +157,9 @@ int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int 
     if (ns < 1) ns = 1;
     pl.num_wg = static_cast<int>(ns * Hkv);
     pl.xcd_skew = ns % 2 == 0 ? skew : 0;     // shares pair up across XCD parities
+    const int pc = opt ? opt->piece_cost : 0;
+    pl.piece_cost = pc == 0 ? kPieceCostTiles * 256 / D / workgroups_per_cu(D, bs)
+                            : (pc < 0 ? 0 : (pc > 1024 ? 1024 : pc));
     pl.records = 2LL * pl.num_wg;
     pl.grid1 = pl.num_wg;
     pl.grid2 = static_cast<long long>(pl.num_wg) * (D / 16 / balanced_slices(D));
@@ -313,6 +323,7 @@ PA_API int paged_attn_plan(const int32_t* seq_lens_host, int num_seqs, int num_h
   info->balanced = pl.balanced ? 1 : 0;
   info->fused = pl.fused ? 1 : 0;
   info->xcd_skew = pl.xcd_skew;
+  info->piece_cost = pl.piece_cost;
   if (seq_lens_host) {
     if (pl.balanced) {
       // host mirror of the device split: sequence s covers tiles [pre_s, pre_s + n)
@@ -320,15 +331,16 @@ PA_API int paged_attn_plan(const int32_t* seq_lens_host, int num_seqs, int num_h
       long long T = 0;
       for (int s = 0; s < num_seqs; ++s) {
         const int L = seq_lens_host[s] < pl.max_seq_len ? seq_lens_host[s] : pl.max_seq_len;
-        T += L > 0 ? (L + 15) / 16 : 0;
+        T += L > 0 ? (L + 15) / 16 + pl.piece_cost : 0;   // virtual tiles
       }
       const long long NS = pl.num_wg / num_kv_heads;
-      const int sk = pl.xcd_skew;
+      const int sk = pl.xcd_skew, pc = pl.piece_cost;
       long long start = 0;
       for (int s = 0; s < num_seqs; ++s) {
         const int L = seq_lens_host[s] < pl.max_seq_len ? seq_lens_host[s] : pl.max_seq_len;
-        const long long n = L > 0 ? (L + 15) / 16 : 0;
-        if (n > 0 && pa::share_holding(T, start, NS, sk) != pa::share_holding(T, start + n - 1, NS, sk))
+        const long long n = L > 0 ? (L + 15) / 16 + pc : 0;   // virtual tiles
+        if (n > 0 && pa::share_holding(T, start + pc, NS, sk) !=
+                         pa::share_holding(T, start + n - 1, NS, sk))
           info->partitioned_seqs++;
         else
           info->single_pass_seqs++;
@@ -394,6 +406,7 @@ PA_API int paged_attn_decode_ex(void* out, const void* q, const void* key_cache,
   args.records = pl.records;
   args.num_wg = pl.num_wg;
   args.xcd_skew = pl.xcd_skew;
+  args.piece_cost = pl.piece_cost;
   args.num_seqs = num_seqs;
   args.num_heads = num_heads;
   args.num_kv_heads = num_kv_heads;

@@ -128,7 +128,12 @@ typedef struct pa_options {
      * equal shares; at most 500.  Share boundaries stay fixed for given sizes, so
      * results do not depend on timing. */
     int xcd_skew;
-    int reserved;
+    /* Length-balanced split only: the tiles of streaming that starting a piece
+     * (a sequence's part inside a share) is counted as when the step is cut into
+     * shares, so shares that start more pieces get fewer tiles.  0 = default
+     * (8 x 256 / head_dim, halved where two workgroups share a CU); negative =
+     * none (equal tiles per share). */
+    int piece_cost;
     /* If non-NULL, hipEventRecord(phase1_begin/phase1_end, stream) is issued
      * immediately before/after the phase-1 kernel (instrumentation only). */
     hipEvent_t phase1_begin;
@@ -152,6 +157,7 @@ typedef struct pa_plan_info {
     int balanced;              /* 1: length-balanced split (partition_size 0) */
     int fused;                 /* 1: partials merged in phase 1, no phase-2 launch */
     int xcd_skew;              /* XCD-paired shares in use (permille), 0 = equal */
+    int piece_cost;            /* balanced split: tiles a piece start counts as */
 } pa_plan_info;
 
 /*

@@ -86,16 +86,21 @@ def test_batch_balanced():
 
 def test_empty_shares_inside_a_sequence():
     """Fewer tiles than shares: empty shares inside the long sequence add identity
-    records, and each draws a ticket."""
+    records, and each draws a ticket.  Without the per-piece lead-in (piece_cost
+    -1), which would add virtual tiles; with it, shares of lead-in tiles only."""
     say("case fused balanced, 48 tiles over 64 shares")
     lens = [16] * 10 + [600]
     w = make(lens, max_blocks_per_seq=4096, partition_size=0, seed=41)
-    info = pa.plan(lens, 24, 4, 256, 16, 4096, 65536, 0, fused_combine=True)
-    assert info["balanced"] == 1 and info["fused"] == 1
-    assert info["active_workgroups"] < info["phase1_workgroups"]     # empty shares exist
-    out = pa.decode(w.q, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, w.scale,
-                    partition_size=0, max_seq_len=65536, fused_combine=True)
-    assert_close(gpu_out(out), oracle_full(w), "fused/empty-shares")
+    for cost in (-1, 0):
+        info = pa.plan(lens, 24, 4, 256, 16, 4096, 65536, 0, fused_combine=True,
+                       piece_cost=cost)
+        assert info["balanced"] == 1 and info["fused"] == 1
+        if cost < 0:
+            assert info["active_workgroups"] < info["phase1_workgroups"]   # empty shares
+        out = pa.decode(w.q, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, w.scale,
+                        partition_size=0, max_seq_len=65536, fused_combine=True,
+                        piece_cost=cost)
+        assert_close(gpu_out(out), oracle_full(w), f"fused/empty-shares/cost{cost}")
 
 
 def test_single_record_segments():

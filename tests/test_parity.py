@@ -354,3 +354,17 @@ def test_xcd_skew_fixed(lens, skew):
     assert info["xcd_skew"] == skew
     out = run(w, P=0, total_tokens_hint=hint, xcd_skew=skew)
     assert_close(gpu_out(out), oracle_full(w), f"xcd/fixed/{lens[0]}/{skew}")
+
+
+@pytest.mark.parametrize("cost", [-1, 3, 8, 60, 1000])
+def test_piece_cost_balanced(cost):
+    """Shares cut with a per-sequence virtual lead-in: with large values many
+    shares hold lead-in tiles only, or cut a sequence right after its lead-in."""
+    say(f"case piece cost {cost}")
+    w = make([5000, 0, 64, 12000, 700, 1, 9000, 33, 20000, 3, 17, 160], seed=90)
+    info = pa.plan(list(w.seq_lens_host), 24, 4, 256, 16, w.max_blocks_per_seq, w.max_seq_len,
+                   0, piece_cost=cost)
+    assert info["balanced"] == 1 and info["piece_cost"] == max(cost, 0)
+    for skew in (-1, 0):
+        out = run(w, P=0, piece_cost=cost, xcd_skew=skew)
+        assert_close(gpu_out(out), oracle_full(w), f"piece_cost/{cost}/skew{skew}")
