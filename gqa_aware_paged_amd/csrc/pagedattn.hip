@@ -137,8 +137,11 @@ int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int 
   const long long slots_all = static_cast<long long>(cus) * workgroups_per_cu(D, bs);
   const bool uniform = hint > 0 && hint == static_cast<long long>(S) * pl.max_seq_len &&
                        static_cast<long long>(S) * pl.units <= slots_all;
+  // the balanced kernel keeps its prefix of (virtual) tiles in 32-bit integers
+  const long long tiles_bound =
+      static_cast<long long>(S) * ((pl.max_seq_len + 15) / 16 + 1024);
   pl.balanced = P_req == 0 && !forced_tier && !uniform && !per_qhead &&
-                S <= pa::kMaxBalancedSeqs;
+                S <= pa::kMaxBalancedSeqs && tiles_bound <= std::numeric_limits<int>::max();
   // XCD-paired shares apply to automatic splits only: explicit partition sizes
   // (the pages' grid) and the per-query-head ablation keep equal partitions
   int skew = opt ? opt->xcd_skew : 0;

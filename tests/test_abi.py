@@ -199,6 +199,9 @@ def test_automatic_partition_size_for_256_cus(lib):
     info = pa.plan([16384] * 1100, 24, 4, 256, 32, 512, 16384, 0)   # too many for the split
     assert info["balanced"] == 0 and info["partition_size"] == 16384
     assert info["partitioned_seqs"] == 0 and info["workspace_bytes"] == 0
+    # a tile prefix beyond 32 bits (1024 x 2^27 tokens): fixed partitions
+    huge = pa.plan(None, 24, 4, 256, 16, 1 << 23, 1 << 27, 0, num_seqs=1024)
+    assert huge["balanced"] == 0
     # equal lengths but more segments (256 x 4) than workgroup slots: balanced split
     info = pa.plan([16384] * 256, 24, 4, 256, 32, 512, 16384, 0, total_tokens_hint=256 * 16384)
     assert info["balanced"] == 1
