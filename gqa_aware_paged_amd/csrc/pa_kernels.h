@@ -24,10 +24,14 @@
 //    fixed partition size; a sequence no longer than the single-pass bound is
 //    one piece (page of commit b80fd2b, three-tier decode dispatch).
 //  - pa_phase1_balanced_kernel: the step's tiles, sequences laid end to end, are
-//    cut into equal shares computed on the device from seq_lens, one workgroup
-//    per (share, KV head).  A sequence inside one share is one pass; a sequence
-//    crossing shares is partitioned at the share boundaries.  Every workgroup
-//    then streams the same number of bytes whatever the length mix.
+//    cut into shares computed on the device from seq_lens, one workgroup per
+//    (share, KV head).  A sequence inside one share is one pass; a sequence
+//    crossing shares is partitioned at the share boundaries.  Each sequence
+//    counts a few virtual tiles for the cost of starting a piece, so every
+//    workgroup has about the same work whatever the length mix.
+// With automatic splits, partitions and shares come in pairs whose members run
+// on XCDs of opposite parity, the even one taking a few percent more (see
+// share_cut): the workgroups of MI355X's odd XCDs stream more slowly.
 //
 // Phase 2 (pa_reduce_kernel) merges the partials of each partitioned segment
 // with the rescale of the online-softmax fix (page of commit 87a19d2): with M

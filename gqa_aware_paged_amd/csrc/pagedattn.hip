@@ -329,8 +329,9 @@ PA_API int paged_attn_plan(const int32_t* seq_lens_host, int num_seqs, int num_h
   info->piece_cost = pl.piece_cost;
   if (seq_lens_host) {
     if (pl.balanced) {
-      // host mirror of the device split: sequence s covers tiles [pre_s, pre_s + n)
-      // of T; share j takes [T*j/NS, T*(j+1)/NS), one workgroup per KV head
+      // host mirror of the device split: sequence s covers virtual tiles
+      // [pre_s, pre_s + piece_cost + n) of T, its real ones last; share j takes
+      // [share_cut(j), share_cut(j + 1)), one workgroup per KV head
       long long T = 0;
       for (int s = 0; s < num_seqs; ++s) {
         const int L = seq_lens_host[s] < pl.max_seq_len ? seq_lens_host[s] : pl.max_seq_len;

@@ -198,7 +198,8 @@ size_t paged_attn_workspace_size_ex(int num_seqs, int num_heads, int num_kv_head
  *   partition_size      tokens per phase-1 partition of a long sequence (a positive
  *                       multiple of 16: the pages' fixed-partition grid), or 0:
  *                       automatic.  Automatic is the length-balanced split (the
- *                       step's tiles cut on the device into equal shares, one
+ *                       step's tiles cut on the device into shares of about equal
+ *                       cost, see pa_options.piece_cost and xcd_skew; one
  *                       workgroup per share and KV head, w per CU as below) for up
  *                       to 1024 sequences; with equal lengths declared through
  *                       pa_options.total_tokens_hint (and no more segments than
