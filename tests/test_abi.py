@@ -327,3 +327,53 @@ def test_xcd_paired_shares_plan(lib):
     # a single partition per sequence has nothing to pair
     assert pa.plan([5000] * 2, 24, 4, 256, 16, 313, 5000, 0, total_tokens_hint=10000,
                    single_pass_max_len=1 << 20)["xcd_skew"] == 0
+
+
+def _split_counts(lens, ns, skew, cost):
+    """Sequences served in one pass / split, for ns shares per KV head cut at
+    floor(T' * (1000 j + skew * (j odd)) / (1000 ns)) over T' virtual tiles, each
+    sequence with tokens counting `cost` lead-in tiles before its real ones."""
+    tiles = [(L + 15) // 16 for L in lens]
+    T = sum(n + cost for n in tiles if n > 0)
+
+    def cut(j):
+        return T if j >= ns else T * (1000 * j + skew * (j & 1)) // (1000 * ns)
+
+    def share(t):
+        return max(j for j in range(ns) if cut(j) <= t)
+
+    single = split = 0
+    start = 0
+    for n in tiles:
+        if n == 0:
+            single += 1
+            continue
+        first, last = start + cost, start + cost + n - 1
+        if share(first) != share(last):
+            split += 1
+        else:
+            single += 1
+        start += n + cost
+    return single, split
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_balanced_cut_matches_formula(lib, seed):
+    """The planner's host mirror of the device cut (start cost + XCD pairing) agrees
+    with the formula written out independently, for random length mixes."""
+    import random
+    rng = random.Random(seed)
+    S = rng.choice([3, 17, 40, 100])
+    lens = [rng.choice([0, rng.randint(1, 300), rng.randint(1, 20000)]) for _ in range(S)]
+    max_len = max(max(lens), 16)
+    mbps = (max_len + 15) // 16
+    for skew, cost in ((-1, -1), (80, 8), (300, 3), (0, 40)):
+        info = pa.plan(lens, 24, 4, 256, 16, mbps, max_len, 0, xcd_skew=skew, piece_cost=cost)
+        assert info["balanced"] == 1
+        ns = info["phase1_workgroups"] // 4
+        sk, pc = info["xcd_skew"], info["piece_cost"]
+        assert pc == (8 if cost == 0 else max(cost, 0))
+        assert sk == (0 if ns % 2 else (80 if skew == 0 else max(skew, 0)))
+        single, split = _split_counts(lens, ns, sk, pc)
+        assert (info["single_pass_seqs"], info["partitioned_seqs"]) == (single, split), \
+            (skew, cost, ns)
