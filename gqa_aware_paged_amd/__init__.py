@@ -291,7 +291,8 @@ def prefill(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     _check(lib().paged_attn_prefill(
         _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(key_cache), _ptr(value_cache),
         _ptr(block_tables), _ptr(ctx_lens), _ptr(query_start), S, Hq, Hkv, D, bs, float(scale),
-        block_tables.shape[1], int(max_query_len), int(max_ctx_len), _DTYPE[q.dtype],
+        block_tables.shape[1], int(max_query_len) if T > 0 else 0, int(max_ctx_len),
+        _DTYPE[q.dtype],
         ctypes.c_void_p(stream)))
     return out
 

@@ -255,7 +255,8 @@ int paged_attn_decode_ex(void* out, const void* q, const void* key_cache,
  *                       values above max_ctx_len are treated as max_ctx_len)
  *   query_start         [num_seqs + 1] int32 (device), non-decreasing, query_start[0] = 0
  *   max_query_len       host-known bound of the chunk lengths (sizes the grid; longer
- *                       chunks are cut to it)
+ *                       chunks are cut to it); 0 (no new tokens) is a no-op, and the
+ *                       row pointers q, k_new, v_new and out may then be NULL
  *   max_ctx_len         host-known bound of ctx_lens, <= max_blocks_per_seq*block_size
  * Shapes, dtypes and alignment as for decode (k_new and v_new 16-byte aligned).
  * No workspace.  Returns PA_OK or the first error found.

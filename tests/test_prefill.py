@@ -90,6 +90,17 @@ def test_empty_chunks_and_no_context():
     assert_close(out, ref(w), "prefill/empty")
 
 
+def test_no_new_tokens_at_all():
+    """Every chunk empty: no rows, so the row tensors are empty (NULL data pointers)
+    whatever bound the caller passes; the call is a no-op."""
+    say("case prefill no new tokens")
+    w = make([58, 0, 300], [0, 0, 0], seed=56)
+    assert w.q.shape[0] == 0
+    out = run(w)                     # passes a bound of 1 with zero rows
+    torch.cuda.synchronize()
+    assert out.shape[0] == 0
+
+
 def test_first_token_without_context_is_value_bitwise():
     say("case prefill first token = V")
     w = make([0, 0], [1, 4], seed=55, poison=False)

@@ -1,7 +1,9 @@
-"""GPU parity over a seeded random sweep of supported configurations: head_dim,
-group size, page size, dtype, length mix (with zero lengths), partition size,
-fused combine, XCD pairing and the per-sequence start cost, in combination.
-Every case is compared with the fp64 oracle to the usual bound."""
+"""GPU parity over a seeded random sweep of supported configurations, in
+combination.  Decode: head_dim, group size, page size, dtype, length mix (with
+zero lengths), partition size, fused combine, XCD pairing and the per-sequence
+start cost.  Prefill: head_dim, group size, page size, dtype, context and chunk
+lengths (with empty ones).  Every case is compared with the fp64 oracle to the
+usual bound."""
 import math
 import random
 
@@ -9,12 +11,14 @@ import pytest
 import torch
 
 import gqa_aware_paged_amd as pa
+import oracle
 import workloads
 from helpers import assert_close, gpu_out, oracle_full, say
 
 pytestmark = pytest.mark.gpu
 
 N_CASES = 120
+N_PREFILL = 60
 
 
 def draw(seed):
@@ -59,3 +63,35 @@ def test_random_config(seed):
                     partition_size=c["P"], max_seq_len=w.max_seq_len, total_tokens_hint=hint,
                     fused_combine=c["fused"], xcd_skew=c["skew"], piece_cost=c["cost"])
     assert_close(gpu_out(out), oracle_full(w), f"random/{seed}")
+
+
+def draw_prefill(seed):
+    rng = random.Random(5000 + seed)
+    D = rng.choice([64, 128, 256])
+    Hkv = rng.choice([1, 2, 4, 8])
+    G = rng.choice([1, 2, 3, 4, 6, 8, 16])
+    while Hkv * G > 64:
+        G //= 2
+    S = rng.choice([1, 2, 3, 6])
+    ctx = [rng.choice([0, rng.randint(1, 64), rng.randint(1, 1500)]) for _ in range(S)]
+    ql = [rng.choice([0, 1, rng.randint(1, 40), rng.randint(1, 200)]) for _ in range(S)]
+    return dict(D=D, Hkv=Hkv, G=G, bs=rng.choice([8, 16, 32, 48, 64]), ctx=ctx, ql=ql,
+                dtype=rng.choice(["f16", "bf16"]))
+
+
+@pytest.mark.parametrize("seed", range(N_PREFILL))
+def test_random_prefill(seed):
+    c = draw_prefill(seed)
+    say(f"case random prefill {seed}: {c}")
+    w = workloads.make_prefill("case", c["ctx"], c["ql"], num_heads=c["Hkv"] * c["G"],
+                               num_kv_heads=c["Hkv"], head_dim=c["D"], block_size=c["bs"],
+                               dtype=c["dtype"], seed=3000 + seed, device="cuda", poison=True)
+    cx = w.ctx
+    out = pa.prefill(w.q, w.k_new, w.v_new, cx.key_cache, cx.value_cache, cx.block_tables,
+                     cx.seq_lens, w.query_start, cx.scale, max(w.max_q_len, 1),
+                     max(cx.max_seq_len, 0))
+    ref = oracle.prefill(w.q, w.k_new, w.v_new, cx.key_cache, cx.value_cache,
+                         cx.block_tables_host, cx.seq_lens_host, w.query_start_host, cx.scale,
+                         cx.dtype)
+    if ref.size:
+        assert_close(gpu_out(out), ref, f"random-prefill/{seed}")
