@@ -40,6 +40,7 @@ constexpr int kMinTilesPerWG = 4;         // balanced mode: at least one tile pe
 // mean workgroup times even out at 80 (odd XCDs ~8-10% slower with equal
 // shares), 258.4 -> 252.2 us/step.
 constexpr int kDefaultXcdSkew = 80;
+constexpr int kCusPerXcd = 32;             // MI355X: 8 XCDs of 32 CUs
 // Balanced mode: tiles of streaming a piece's start costs (head_dim 256, one
 // workgroup per CU).  Measured on 32 x U[512, 8192] with equal shares: a share
 // holding two pieces ran 4.8 us (about 8 tiles) longer than one holding one.
@@ -147,6 +148,8 @@ int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int 
   int skew = opt ? opt->xcd_skew : 0;
   skew = skew == 0 ? kDefaultXcdSkew : (skew < 0 ? 0 : (skew > 500 ? 500 : skew));
   if (P_req != 0 || per_qhead) skew = 0;
+  // a single-XCD partition of the device (32 CUs) has no second parity to pair with
+  if (cus < 2 * kCusPerXcd) skew = 0;
   if (pl.balanced) {
     // shares x KV heads: workgroups_per_cu resident workgroups per CU (measured on
     // the batch and long workloads as for fixed partitions: one per CU at head_dim

@@ -321,6 +321,9 @@ def test_xcd_paired_shares_plan(lib):
     assert pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0, total_tokens_hint=4 * L,
                    per_query_head=True)["xcd_skew"] == 0
     assert pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0)["xcd_skew"] == 80
+    # a single-XCD partition (32 CUs) has nothing to pair across
+    assert pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0, num_cus=32)["xcd_skew"] == 0
+    assert pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0, num_cus=64)["xcd_skew"] == 80
     # an odd number of shares per KV head cannot pair up
     odd = pa.plan([40] * 3, 24, 4, 256, 16, 3, 40, 0)
     assert odd["balanced"] == 1 and odd["phase1_workgroups"] == 4 * 3 and odd["xcd_skew"] == 0
