@@ -125,8 +125,8 @@ typedef struct pa_options {
      * stream K/V ~8-10% slower than those of the even ones, so shares are paired
      * across XCD parities and the even member takes this many permille of the
      * pair's mean more (the odd one as many less).  0 = default (80); negative =
-     * equal shares; at most 500; off when num_cus is below 64 (one XCD).  Share boundaries stay fixed for given sizes, so
-     * results do not depend on timing. */
+     * equal shares; at most 500; off when num_cus is below 64 (one XCD).  Share
+     * boundaries stay fixed for given sizes, so results do not depend on timing. */
     int xcd_skew;
     /* Length-balanced split only: the tiles of streaming that starting a piece
      * (a sequence's part inside a share) is counted as when the step is cut into
