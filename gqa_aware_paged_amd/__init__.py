@@ -20,7 +20,8 @@ PA_F16, PA_BF16 = 0, 1
 _DTYPE = {torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 SYMBOLS = ("paged_attn_workspace_size", "paged_attn_workspace_size_ex", "paged_attn_decode",
            "paged_attn_decode_ex", "paged_attn_status_str", "paged_attn_plan",
-           "paged_attn_gather_probe", "paged_attn_workspace_init", "paged_attn_prefill")
+           "paged_attn_gather_probe", "paged_attn_workspace_init", "paged_attn_prefill",
+           "paged_attn_decode_noalloc")
 
 
 class Options(ctypes.Structure):
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_prefill.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, I,
                                          I, P]
         L.paged_attn_prefill.restype = I
+        L.paged_attn_decode_noalloc.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, P, I, I, I]
+        L.paged_attn_decode_noalloc.restype = I
         _lib = L
     return _lib
 
@@ -262,6 +265,27 @@ def decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
         ctypes.c_void_p(stream), mbps, int(max_seq_len), _DTYPE[q.dtype],
         0 if workspace is None else workspace.numel() * workspace.element_size(),
         ctypes.byref(o)))
+    return out
+
+
+def decode_noalloc(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                   block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                   out: torch.Tensor, partition_size: int = 0, max_seq_len: int = 0,
+                   stream: Optional[int] = None) -> torch.Tensor:
+    """paged_attn_decode_noalloc: one decode step with the library's device-resident
+    workspace (no allocation in the call; `out` is the caller's).  Calls that overlap
+    on one GPU share that workspace and must be serialised by the caller."""
+    _validate(q, key_cache, value_cache, block_tables, seq_lens)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    S, Hq, D = q.shape
+    _, Hkv, bs, _ = key_cache.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib().paged_attn_decode_noalloc(
+        _ptr(out), _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(seq_lens), S, Hq, Hkv, D, bs, float(scale), int(partition_size),
+        ctypes.c_void_p(stream), block_tables.shape[1], int(max_seq_len), _DTYPE[q.dtype]))
     return out
 
 

@@ -12,6 +12,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <limits>
@@ -450,6 +451,65 @@ PA_API int paged_attn_decode(void* out, const void* q, const void* key_cache,
                               num_heads, num_kv_heads, head_dim, block_size, scale,
                               partition_size, workspace, stream, max_blocks_per_seq,
                               max_seq_len, dtype, workspace_bytes, nullptr);
+}
+
+namespace {
+
+// Workspace of paged_attn_decode_noalloc: a file-scope device array, one copy per
+// GPU the library runs on, held until the process ends.  Host code never uses its
+// name as an address (on the host it is only a stand-in): the device address is
+// taken once per device with hipGetSymbolAddress and kept in scratch_addr.
+constexpr size_t kScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_addr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first call
+// made with that device current).
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_HIP;
+  void* p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return PA_ERR_HIP;
+    scratch_addr[dev].store(p, std::memory_order_release);   // racing lookups store the same value
+  }
+  *out = p;
+  return PA_OK;
+}
+
+}  // namespace
+
+PA_API int paged_attn_decode_noalloc(void* out, const void* q, const void* key_cache,
+                                     const void* value_cache, const int32_t* block_tables,
+                                     const int32_t* seq_lens, int num_seqs, int num_heads,
+                                     int num_kv_heads, int head_dim, int block_size, float scale,
+                                     int partition_size, hipStream_t stream,
+                                     int max_blocks_per_seq, int max_seq_len, int dtype) {
+  int st = check_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       max_blocks_per_seq, max_seq_len, partition_size, dtype);
+  if (st != PA_OK) return st;
+  if (!std::isfinite(scale)) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  Plan pl;
+  st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                 max_seq_len, partition_size, nullptr, pl);
+  if (st != PA_OK) return st;
+  if (pl.ws_bytes > kScratchBytes) return PA_ERR_WORKSPACE;
+  // Every region this plan reads (partial records, balanced jobs) is written by the
+  // same call before it is read, so the array needs no clearing between calls; the
+  // ticket area is used only by the fused combine, which this entry point never runs.
+  void* ws = nullptr;
+  if (pl.ws_bytes > 0) {
+    st = scratch_on_current_device(&ws);
+    if (st != PA_OK) return st;
+  }
+  return paged_attn_decode_ex(out, q, key_cache, value_cache, block_tables, seq_lens, num_seqs,
+                              num_heads, num_kv_heads, head_dim, block_size, scale,
+                              partition_size, ws, stream, max_blocks_per_seq, max_seq_len, dtype,
+                              pl.ws_bytes > 0 ? kScratchBytes : 0, nullptr);
 }
 
 PA_API int paged_attn_workspace_init(void* workspace, size_t workspace_bytes,

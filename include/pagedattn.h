@@ -30,8 +30,10 @@
  *   - All tensor pointers are DEVICE pointers unless a parameter says "host".
  *   - The caller owns every buffer.  The library never allocates or frees device
  *     memory, never synchronises the device or the stream, and keeps no pointer
- *     after returning.  It has no mutable global state: concurrent calls on
- *     different streams are safe when their `out` and `workspace` differ.
+ *     after returning.  Apart from paged_attn_decode_noalloc's per-device scratch
+ *     array and the cache of its address, it has no mutable global state:
+ *     concurrent calls on different streams are safe when their `out` and
+ *     `workspace` differ.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *     and runs asynchronously.  All host-side validation happens before the
  *     first HIP call; a rejected call enqueues nothing.
@@ -71,6 +73,9 @@ extern "C" {
 /* Bytes at the start of every non-empty workspace reserved for the ticket
  * counters of the fused combine (pa_options.fused_combine). */
 #define PA_WORKSPACE_TICKET_BYTES 65536
+
+/* Size of the device-resident workspace of paged_attn_decode_noalloc (per GPU). */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
 typedef enum pa_dtype_t {
     PA_F16 = 0,
@@ -268,6 +273,31 @@ int paged_attn_prefill(void* out, const void* q, const void* k_new, const void* 
                        int num_kv_heads, int head_dim, int block_size, float scale,
                        int max_blocks_per_seq, int max_query_len, int max_ctx_len, int dtype,
                        hipStream_t stream);
+
+/*
+ * paged_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, plan, kernels and results as
+ * paged_attn_decode with the same sizes (and no options); the workspace is a
+ * file-scope device array of PA_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held
+ * until the process ends, whose address is looked up (hipGetSymbolAddress) on the
+ * first call made with a device current.  The call allocates nothing and calls no
+ * allocating routine.  Work runs on the current device: `stream` must belong to it.
+ * A plan needing more than PA_NOALLOC_SCRATCH_BYTES of workspace (the bound covers
+ * every plan of partition_size 0 with up to 1024 sequences; explicit partition
+ * sizes need num_seqs * num_kv_heads * ceil(max_seq_len / partition_size) *
+ * (num_heads / num_kv_heads) * (4 * head_dim + 8) bytes plus 64 KiB) returns
+ * PA_ERR_WORKSPACE before any work is enqueued.  Every region a call reads is
+ * written by that call first, so nothing needs clearing between calls; calls that
+ * overlap on one GPU (other streams, other host threads) share the array and race:
+ * the caller serialises them.  Returns PA_OK or the first error found.
+ */
+int paged_attn_decode_noalloc(void* out, const void* q, const void* key_cache,
+                              const void* value_cache, const int32_t* block_tables,
+                              const int32_t* seq_lens, int num_seqs, int num_heads,
+                              int num_kv_heads, int head_dim, int block_size, float scale,
+                              int partition_size, hipStream_t stream, int max_blocks_per_seq,
+                              int max_seq_len, int dtype);
 
 /*
  * Clears the ticket area (the first min(workspace_bytes,
