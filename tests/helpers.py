@@ -1,4 +1,5 @@
 """Shared helpers of the GPU parity tests."""
+import os
 import sys
 
 import numpy as np
@@ -8,6 +9,10 @@ import oracle
 
 ATOL = 2e-3      # absolute bound on fp16/bf16 outputs (fp32 accumulate)
 RTOL = 1e-2      # relative bound
+
+# One entry per assert_close call: (test id, case, max_abs, max_rel, worst err/tol).
+# tests/conftest.py prints the worst case per test file at the end of the run.
+MARGINS = []
 
 
 def say(msg: str):
@@ -25,9 +30,14 @@ def assert_close(got: np.ndarray, ref: np.ndarray, what: str = ""):
     tol = np.maximum(ATOL, RTOL * np.abs(ref))
     bad = err > tol
     rel = err / np.maximum(np.abs(ref), 1e-30)
-    say(f"  {what}: max_abs={err.max():.3e} max_rel(|ref|>1e-2)="
-        f"{(rel[np.abs(ref) > 1e-2].max() if (np.abs(ref) > 1e-2).any() else 0):.3e} "
-        f"n={got.size}")
+    big = np.abs(ref) > 1e-2
+    max_rel = float(rel[big].max()) if big.any() else 0.0
+    max_abs = float(err.max()) if err.size else 0.0
+    ratio = float((err / tol).max()) if err.size else 0.0
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    MARGINS.append((test, what, max_abs, max_rel, ratio))
+    say(f"  {what}: max_abs={max_abs:.3e} max_rel(|ref|>1e-2)={max_rel:.3e} "
+        f"worst err/tol={ratio:.3f} n={got.size}")
     if bad.any():
         i = np.unravel_index(np.argmax(err - tol), err.shape)
         raise AssertionError(f"{what}: {int(bad.sum())} elements out of tolerance; worst at {i}: "
