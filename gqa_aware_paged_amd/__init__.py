@@ -21,7 +21,7 @@ _DTYPE = {torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 SYMBOLS = ("paged_attn_workspace_size", "paged_attn_workspace_size_ex", "paged_attn_decode",
            "paged_attn_decode_ex", "paged_attn_status_str", "paged_attn_plan",
            "paged_attn_gather_probe", "paged_attn_workspace_init", "paged_attn_prefill",
-           "paged_attn_decode_noalloc")
+           "paged_attn_decode_noalloc", "paged_attn_read_probe")
 
 
 class Options(ctypes.Structure):
@@ -29,7 +29,8 @@ class Options(ctypes.Structure):
                 ("total_tokens_hint", ctypes.c_longlong), ("per_query_head", ctypes.c_int),
                 ("fused_combine", ctypes.c_int), ("xcd_skew", ctypes.c_int),
                 ("piece_cost", ctypes.c_int),
-                ("phase1_begin", ctypes.c_void_p), ("phase1_end", ctypes.c_void_p)]
+                ("phase1_begin", ctypes.c_void_p), ("phase1_end", ctypes.c_void_p),
+                ("stream_walk", ctypes.c_int)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -41,7 +42,8 @@ class PlanInfo(ctypes.Structure):
                 ("partitioned_seqs", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t),
                 ("threads_per_workgroup", ctypes.c_int), ("lds_bytes_phase1", ctypes.c_int),
                 ("balanced", ctypes.c_int), ("fused", ctypes.c_int),
-                ("xcd_skew", ctypes.c_int), ("piece_cost", ctypes.c_int)]
+                ("xcd_skew", ctypes.c_int), ("piece_cost", ctypes.c_int),
+                ("stream", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -82,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_prefill.restype = I
         L.paged_attn_decode_noalloc.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, P, I, I, I]
         L.paged_attn_decode_noalloc.restype = I
+        L.paged_attn_read_probe.argtypes = [P, Z, P, ctypes.c_longlong, I, P, P]
+        L.paged_attn_read_probe.restype = I
         _lib = L
     return _lib
 
@@ -100,8 +104,9 @@ def _check(status: int):
 def _opts(single_pass_max_len: Optional[int], num_cus: int = 0,
           events: Optional[Tuple[int, int]] = None, total_tokens_hint: int = 0,
           per_query_head: bool = False, fused_combine: bool = False,
-          xcd_skew: int = 0, piece_cost: int = 0) -> Options:
+          xcd_skew: int = 0, piece_cost: int = 0, stream_walk: int = 0) -> Options:
     o = Options()
+    o.stream_walk = int(stream_walk)
     o.xcd_skew = int(xcd_skew)
     o.piece_cost = int(piece_cost)
     o.per_query_head = 1 if per_query_head else 0
@@ -123,7 +128,7 @@ def plan(seq_lens_host, num_heads: int, num_kv_heads: int, head_dim: int, block_
          dtype: int = PA_F16, single_pass_max_len: Optional[int] = None,
          num_seqs: Optional[int] = None, num_cus: int = 0, total_tokens_hint: int = 0,
          per_query_head: bool = False, fused_combine: bool = False,
-         xcd_skew: int = 0, piece_cost: int = 0) -> dict:
+         xcd_skew: int = 0, piece_cost: int = 0, stream_walk: int = 0) -> dict:
     """Host-only plan (no GPU needed).  seq_lens_host: sequence of ints or None."""
     arr = None
     if seq_lens_host is not None:
@@ -133,7 +138,7 @@ def plan(seq_lens_host, num_heads: int, num_kv_heads: int, head_dim: int, block_
     info = PlanInfo()
     o = _opts(single_pass_max_len, num_cus, total_tokens_hint=total_tokens_hint,
               per_query_head=per_query_head, fused_combine=fused_combine, xcd_skew=xcd_skew,
-              piece_cost=piece_cost)
+              piece_cost=piece_cost, stream_walk=stream_walk)
     _check(lib().paged_attn_plan(arr, int(num_seqs or 0), num_heads, num_kv_heads, head_dim,
                                  block_size, max_blocks_per_seq, max_seq_len, partition_size,
                                  dtype, ctypes.byref(o), ctypes.byref(info)))
@@ -144,9 +149,11 @@ def workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: i
                    block_size: int, max_blocks_per_seq: int, max_seq_len: int = 0,
                    partition_size: int = 0, single_pass_max_len: Optional[int] = None,
                    total_tokens_hint: int = 0, num_cus: int = 0,
-                   per_query_head: bool = False) -> int:
+                   per_query_head: bool = False, stream_walk: int = 0,
+                   fused_combine: bool = False) -> int:
     o = _opts(single_pass_max_len, num_cus, total_tokens_hint=total_tokens_hint,
-              per_query_head=per_query_head)
+              per_query_head=per_query_head, stream_walk=stream_walk,
+              fused_combine=fused_combine)
     n = lib().paged_attn_workspace_size_ex(num_seqs, num_heads, num_kv_heads, head_dim,
                                            block_size, max_blocks_per_seq, max_seq_len,
                                            partition_size, ctypes.byref(o))
@@ -179,7 +186,7 @@ class Decoder:
                  single_pass_max_len: Optional[int] = None, total_tokens_hint: int = 0,
                  num_cus: int = 0, per_query_head: bool = False,
                  fused_combine: bool = False, xcd_skew: int = 0, piece_cost: int = 0,
-                 device="cuda"):
+                 stream_walk: int = 0, device="cuda"):
         self.shape = (num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                       max_blocks_per_seq)
         self.dtype = dtype
@@ -187,11 +194,11 @@ class Decoder:
         self.partition_size = int(partition_size)
         self.opts = _opts(single_pass_max_len, num_cus, total_tokens_hint=total_tokens_hint,
                           per_query_head=per_query_head, fused_combine=fused_combine,
-                          xcd_skew=xcd_skew, piece_cost=piece_cost)
+                          xcd_skew=xcd_skew, piece_cost=piece_cost, stream_walk=stream_walk)
         nbytes = workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                                 max_blocks_per_seq, max_seq_len, partition_size,
                                 single_pass_max_len, total_tokens_hint, num_cus,
-                                per_query_head)
+                                per_query_head, stream_walk, fused_combine)
         self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
         self.workspace_bytes = nbytes
         if fused_combine and nbytes > 0:
@@ -238,7 +245,7 @@ def decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
            workspace: Optional[torch.Tensor] = None, single_pass_max_len: Optional[int] = None,
            events: Optional[Tuple[int, int]] = None, total_tokens_hint: int = 0,
            per_query_head: bool = False, fused_combine: bool = False,
-           xcd_skew: int = 0, piece_cost: int = 0) -> torch.Tensor:
+           xcd_skew: int = 0, piece_cost: int = 0, stream_walk: int = 0) -> torch.Tensor:
     """One decode step: out[s,h] = softmax(scale q K^T) V over the paged caches.
 
     fused_combine: merge partitions inside phase 1; a workspace passed in must then
@@ -248,7 +255,8 @@ def decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
     _, Hkv, bs, _ = key_cache.shape
     mbps = block_tables.shape[1]
     need = workspace_size(S, Hq, Hkv, D, bs, mbps, max_seq_len, partition_size,
-                          single_pass_max_len, total_tokens_hint, 0, per_query_head)
+                          single_pass_max_len, total_tokens_hint, 0, per_query_head,
+                          stream_walk, fused_combine)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         if fused_combine:
@@ -257,7 +265,7 @@ def decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
         out = torch.empty_like(q)
     o = _opts(single_pass_max_len, events=events, total_tokens_hint=total_tokens_hint,
               per_query_head=per_query_head, fused_combine=fused_combine, xcd_skew=xcd_skew,
-              piece_cost=piece_cost)
+              piece_cost=piece_cost, stream_walk=stream_walk)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(lib().paged_attn_decode_ex(
         _ptr(out), _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
@@ -319,6 +327,28 @@ def prefill(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
         _DTYPE[q.dtype],
         ctypes.c_void_p(stream)))
     return out
+
+
+def read_probe(src: torch.Tensor, chunk_bytes: int, order: Optional[torch.Tensor] = None,
+               num_workgroups: int = 256, sink: Optional[torch.Tensor] = None,
+               stream: Optional[int] = None) -> torch.Tensor:
+    """Read every chunk of `src` (a device tensor of whole chunks) once, in order or
+    in the order of `order` (device int64 permutation of the chunk indices); returns
+    the per-workgroup XOR folds."""
+    nbytes = src.numel() * src.element_size()
+    if nbytes % chunk_bytes:
+        raise ValueError("src must hold whole chunks")
+    n = nbytes // chunk_bytes
+    if order is not None:
+        if order.dtype != torch.int64 or order.numel() != n or not order.is_cuda:
+            raise ValueError("order must be a device int64 tensor with one entry per chunk")
+    if sink is None:
+        sink = torch.empty(num_workgroups, dtype=torch.int32, device=src.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(src.device).cuda_stream
+    _check(lib().paged_attn_read_probe(_ptr(src), chunk_bytes, _ptr(order), n, num_workgroups,
+                                       _ptr(sink), ctypes.c_void_p(stream)))
+    return sink
 
 
 def gather_probe(key_cache: torch.Tensor, value_cache: torch.Tensor,

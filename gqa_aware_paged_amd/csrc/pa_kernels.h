@@ -990,23 +990,29 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_balanced_kernel(Decod
 // ---------------------------------------------------------------------------
 constexpr int kRedThreads = 256;
 constexpr int kRedWaves = kRedThreads / 64;
+// partials of every head a thread of pa_reduce_kernel loads per round
+__host__ __device__ constexpr int reduce_unroll(int G) {
+  return G >= 16 ? 1 : (G >= 6 ? 2 : (G >= 3 ? 4 : 8));
+}
 
 // Workgroup = (segment, SPW consecutive 16-wide head_dim slices).  Thread
 // (pg, ql) covers head_dim values 4*ql .. +3 of the workgroup's slices and folds
 // partials p = pg, pg + PG, ... of every head into a running partial, issuing all
 // loads of a round (G heads x U partials) before consuming any; the PG groups are
-// then combined with the same rule by lane shuffles and through LDS.
-//   grid mode (BAL = false): workgroup (segment q, slice group), partials
-//     q*max_parts + p for p < ceil(L/P); segments in one pass are skipped.
-//   balanced mode (BAL = true): workgroup (w, slice group) merges the segment
-//     begun by phase-1 workgroup w, if any: record 2w+1, then 2(w+p*Hkv) for
-//     p >= 1 (the same KV head in the following shares).
-template <int D, class DT, int G, int SPW, bool BAL>
+// then combined with the same rule by lane shuffles and through LDS.  SPW = 1
+// spreads a segment over D/16 workgroups of up to PG*U = 64*U partials a round, for
+// many partials per segment; a larger SPW takes fewer, wider workgroups.
+//   fixed partitions (a.jobs == nullptr): workgroup (segment q, slice group),
+//     partials q*max_parts + p for p < ceil(L/P); segments in one pass are skipped.
+//   balanced split: workgroup (w, slice group) merges the segment begun by phase-1
+//     workgroup w, if any: record 2w+1, then 2(w+p*Hkv) for p >= 1 (the same KV
+//     head in the following shares).
+template <int D, class DT, int G, int SPW>
 __global__ __launch_bounds__(kRedThreads) void pa_reduce_kernel(DecodeArgs a) {
   constexpr int NSG = D / 16 / SPW;        // slice groups per segment
   constexpr int QL = 4 * SPW;              // float4 lanes per partial group
   constexpr int PG = kRedThreads / QL;     // partial groups
-  constexpr int U = G >= 16 ? 1 : (G >= 6 ? 2 : (G >= 3 ? 4 : 8));
+  constexpr int U = reduce_unroll(G);
   static_assert(QL <= 64, "a partial group must fit in a wave");
   __shared__ float red_m[kRedWaves][G][QL], red_w[kRedWaves][G][QL];
   __shared__ f32x4 red_a[kRedWaves][G][QL];
@@ -1020,7 +1026,7 @@ __global__ __launch_bounds__(kRedThreads) void pa_reduce_kernel(DecodeArgs a) {
 
   int q, np;
   long long rec0, step, first;
-  if constexpr (BAL) {
+  if (a.jobs != nullptr) {
     const int2 job = a.jobs[slot];
     if (job.x < 0) return;
     q = job.x;
@@ -1143,6 +1149,59 @@ __global__ __launch_bounds__(256) void pa_gather_kernel(GatherArgs a) {
         reinterpret_cast<u32x4*>(a.v_out + dst)[c] = rv[j];
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Read probe: what the box delivers to the decode's access pattern.  The pages'
+// case for the KV-head grid is the K/V bytes read (page of commit 8d26e23, "Key
+// design change"), so the decode is bounded by read bandwidth; this kernel reads
+// n chunks of CB bytes (one (page, KV head) block of the caches: 8 KiB at 16
+// tokens x head_dim 256) with the phase-1 load form (nontemporal 16-byte loads,
+// 1 KiB contiguous per instruction), in order or in the order of a permutation,
+// two chunks in flight per wave, folds them with XOR and writes one word per
+// workgroup.  Workgroup b takes chunks [n*b/grid, n*(b+1)/grid), wave w every
+// fourth of them starting at w.
+// ---------------------------------------------------------------------------
+template <int CB>
+__global__ __launch_bounds__(256) void pa_read_probe_kernel(const u32x4* __restrict__ src,
+                                                            const long long* order, long long n,
+                                                            unsigned* sink) {
+  constexpr int NL = CB / 1024;             // loads per lane per chunk
+  typedef const __attribute__((address_space(4))) long long const_i64;
+  __shared__ unsigned fold[256];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long long c0 = n * blockIdx.x / gridDim.x, c1 = n * (blockIdx.x + 1) / gridDim.x;
+  u32x4 acc = {0, 0, 0, 0};
+  auto load = [&](long long c, u32x4 (&d)[NL]) {
+    const long long id = order ? ((const_i64*)order)[c] : c;
+    const u32x4* p = src + id * (CB / 16);
+#pragma unroll
+    for (int j = 0; j < NL; ++j) d[j] = __builtin_nontemporal_load(p + j * 64 + lane);
+  };
+  auto consume = [&](const u32x4 (&d)[NL]) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) acc ^= d[j];
+  };
+  u32x4 ra[NL], rb[NL];
+  long long c = c0 + wave;
+  if (c < c1) load(c, ra);
+  if (c + 4 < c1) load(c + 4, rb);
+  for (; c < c1; c += 8) {
+    consume(ra);
+    if (c + 8 < c1) load(c + 8, ra);
+    if (c + 4 < c1) {
+      consume(rb);
+      if (c + 12 < c1) load(c + 12, rb);
+    }
+  }
+  fold[threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned x = 0;
+    for (int i = 0; i < 256; ++i) x ^= fold[i];
+    sink[blockIdx.x] = x;
   }
 }
 

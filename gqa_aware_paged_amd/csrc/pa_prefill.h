@@ -163,7 +163,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void pa_pref
     else return i * (NT / (8 * CH)) + wave / (CH / 8);
   };
   // a (page, KV head) block of the cache is page_bytes long; the rows of KV head
-  // kvh start kvh_bytes into it (both below 2^32 for every supported shape)
+  // kvh start kvh_bytes into it (paged_attn_prefill rejects shapes where
+  // num_kv_heads * max(block_size, 32) * head_dim * 2 reaches 2^32, so both fit)
   const unsigned row_bytes = 2u * D;
   const unsigned kvh_bytes = static_cast<unsigned>(kvh) * static_cast<unsigned>(bs) * row_bytes;
   const unsigned page_bytes = static_cast<unsigned>(Hkv) * static_cast<unsigned>(bs) * row_bytes;

@@ -16,9 +16,11 @@
 #include <cmath>
 #include <cstdint>
 #include <limits>
+#include <vector>
 
 #include "pa_kernels.h"
 #include "pa_prefill.h"
+#include "pa_stream.h"
 
 #define PA_API extern "C" __attribute__((visibility("default")))
 
@@ -48,6 +50,9 @@ constexpr int kCusPerXcd = 32;             // MI355X: 8 XCDs of 32 CUs
 // Scaled to other head sizes (a tile carries head_dim/256 of the bytes) and
 // halved with two workgroups per CU (each streams at half the rate).
 constexpr int kPieceCostTiles = 8;
+// Per-wave streams: a piece that starts inside a wave's run costs a state flush and,
+// for a new sequence, query rows loaded with its first tile; counted as one tile.
+constexpr int kStreamPieceCost = 1;
 constexpr int kBalancedSlices = 8;        // balanced phase 2: 16-wide slices per workgroup
 
 // 16-wide head_dim slices one balanced phase-2 workgroup merges
@@ -55,6 +60,8 @@ constexpr int balanced_slices(int D) { return D / 16 < kBalancedSlices ? D / 16 
 
 struct Plan {
   bool balanced = false; // length-balanced split (partition_size 0) vs fixed partitions
+  bool stream = false;   // phase 1 as per-wave streams (pa_phase1_stream_kernel)
+  bool parts = false;    // stream kernel with an explicit partition size
   int P = 0;             // partition size (tokens), grid mode
   int T1 = 0;            // single-pass threshold (tokens), grid mode
   int max_parts = 0;     // partitions per (seq, kv head) slot; 0 = no phase 2, grid mode
@@ -67,6 +74,7 @@ struct Plan {
   long long records = 0; // partial records in the workspace
   long long grid1 = 0, grid2 = 0;
   bool fused = false;    // partials merged in phase 1 (ticket counters), no phase 2
+  bool wide_reduce = false;  // phase 2 takes balanced_slices(D) slices per workgroup
   size_t ws_acc_off = 0, ws_ml_off = 0, ws_jobs_off = 0, ws_bytes = 0;
 };
 
@@ -101,6 +109,11 @@ int check_sizes(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, in
 // second resident workgroup hides the per-tile latency (head_dim 64: 3.2 -> 5.4
 // TB/s; 128: 4.7 -> 6.1; 8-token pages: 5.0 -> 5.9).
 int workgroups_per_cu(int D, int bs) { return D >= 256 && bs >= 16 ? 1 : 2; }
+
+// Resident workgroups per CU of the stream kernel: its LDS (tile slots, the parked
+// states of three waves, the per-sequence prefixes) is 124 KiB at head_dim 256, so
+// one; at head_dim 128 or 64 two.
+int stream_workgroups_per_cu(int D) { return D >= 256 ? 1 : 2; }
 
 // Fixed partition size when the caller passes 0 but the balanced split does not
 // apply (equal lengths declared, a forced tier, or more sequences than it keeps
@@ -140,37 +153,75 @@ int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int 
   const bool uniform = hint > 0 && hint == static_cast<long long>(S) * pl.max_seq_len &&
                        static_cast<long long>(S) * pl.units <= slots_all;
   // the balanced kernel keeps its prefix of (virtual) tiles in 32-bit integers
-  const long long tiles_bound =
-      static_cast<long long>(S) * ((pl.max_seq_len + 15) / 16 + 1024);
+  const long long max_tiles = (pl.max_seq_len + 15) / 16;
+  const long long tiles_bound = static_cast<long long>(S) * (max_tiles + 1024);
   pl.balanced = P_req == 0 && !forced_tier && !uniform && !per_qhead &&
                 S <= pa::kMaxBalancedSeqs && tiles_bound <= std::numeric_limits<int>::max();
-  // XCD-paired shares apply to automatic splits only: explicit partition sizes
-  // (the pages' grid) and the per-query-head ablation keep equal partitions
+  // per-wave streams (the balanced split, and explicit partition sizes): not with the
+  // fused combine or the per-query-head ablation, which keep one workgroup per piece
+  const bool stream_ok = !(opt && opt->stream_walk < 0) && !per_qhead &&
+                         !(opt && opt->fused_combine) && S <= pa::kMaxBalancedSeqs;
+  const int pc_req = opt ? opt->piece_cost : 0;
+  const int stream_pc = pc_req == 0 ? kStreamPieceCost : (pc_req < 0 ? 0 : (pc_req > 1024 ? 1024 : pc_req));
+  int parts_T1 = 0;
+  long long parts_max = 1;       // partitions of the longest sequence
+  bool stream_parts = false;
+  if (stream_ok && P_req > 0) {
+    parts_T1 = forced_tier ? opt->single_pass_max_len : P_req;
+    const long long P16 = P_req / 16;
+    parts_max = pl.max_seq_len > parts_T1 ? (max_tiles + P16 - 1) / P16 : 1;
+    // the kernel keeps virtual tiles (partitions x piece cost + tiles) in 32 bits
+    stream_parts = static_cast<long long>(S) * (max_tiles + parts_max * stream_pc) <=
+                   std::numeric_limits<int>::max();
+  }
+  // XCD-paired shares apply to automatic splits, and to the shares (not the
+  // partitions) of explicit partition sizes on per-wave streams; the pages' dense
+  // grid and the per-query-head ablation keep equal work per workgroup
   int skew = opt ? opt->xcd_skew : 0;
   skew = skew == 0 ? kDefaultXcdSkew : (skew < 0 ? 0 : (skew > 500 ? 500 : skew));
-  if (P_req != 0 || per_qhead) skew = 0;
+  if (per_qhead || (P_req != 0 && !stream_parts)) skew = 0;
   // a single-XCD partition of the device (32 CUs) has no second parity to pair with
   if (cus < 2 * kCusPerXcd) skew = 0;
   if (pl.balanced) {
+    pl.stream = stream_ok;
     // shares x KV heads: workgroups_per_cu resident workgroups per CU (measured on
     // the batch and long workloads as for fixed partitions: one per CU at head_dim
     // 256 with 16-token pages, 4% faster cold on the batch than two), but at least
     // kMinTilesPerWG tiles per workgroup
-    const long long tiles = static_cast<long long>(S) * ((pl.max_seq_len + 15) / 16);
+    const long long tiles = static_cast<long long>(S) * max_tiles;
     long long ns = (tiles + kMinTilesPerWG - 1) / kMinTilesPerWG;
-    const long long slots = static_cast<long long>(cus) * workgroups_per_cu(D, bs);
+    const long long slots = static_cast<long long>(cus) *
+                            (pl.stream ? stream_workgroups_per_cu(D) : workgroups_per_cu(D, bs));
     const long long ns_max = slots / Hkv > 0 ? slots / Hkv : 1;
     if (ns > ns_max) ns = ns_max;
     if (ns < 1) ns = 1;
     pl.num_wg = static_cast<int>(ns * Hkv);
     pl.xcd_skew = ns % 2 == 0 ? skew : 0;     // shares pair up across XCD parities
-    const int pc = opt ? opt->piece_cost : 0;
-    pl.piece_cost = pc == 0 ? kPieceCostTiles * 256 / D / workgroups_per_cu(D, bs)
-                            : (pc < 0 ? 0 : (pc > 1024 ? 1024 : pc));
+    pl.piece_cost = pl.stream ? stream_pc
+                    : pc_req == 0 ? kPieceCostTiles * 256 / D / workgroups_per_cu(D, bs)
+                                  : (pc_req < 0 ? 0 : (pc_req > 1024 ? 1024 : pc_req));
     pl.records = 2LL * pl.num_wg;
     pl.grid1 = pl.num_wg;
     pl.grid2 = static_cast<long long>(pl.num_wg) * (D / 16 / balanced_slices(D));
+    pl.wide_reduce = true;
     pl.T1 = -1;
+  } else if (stream_parts) {
+    // the pages' partitions of P tokens, one partial each, walked by per-wave streams
+    // over shares that end on partition boundaries
+    pl.stream = pl.parts = true;
+    pl.P = P_req;
+    pl.T1 = parts_T1;
+    if (pl.max_seq_len > pl.T1) pl.max_parts = (pl.max_seq_len + pl.P - 1) / pl.P;
+    const long long slots = static_cast<long long>(cus) * stream_workgroups_per_cu(D);
+    long long ns = slots / Hkv > 0 ? slots / Hkv : 1;
+    const long long pieces = static_cast<long long>(S) * parts_max;
+    if (ns > pieces) ns = pieces;
+    if (ns < 1) ns = 1;
+    pl.num_wg = static_cast<int>(ns * Hkv);
+    pl.xcd_skew = ns % 2 == 0 ? skew : 0;
+    pl.piece_cost = stream_pc;
+    pl.grid1 = pl.num_wg;
+    pl.records = static_cast<long long>(S) * pl.units * pl.max_parts;
   } else {
     pl.P = P_req > 0 ? P_req
                      : auto_partition(S, pl.units, pl.max_seq_len,
@@ -182,8 +233,15 @@ int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int 
     pl.xcd_skew = pl.max_parts >= 2 ? skew : 0;
     const long long parts = pl.max_parts > 0 ? pl.max_parts : 1;
     pl.grid1 = static_cast<long long>(S) * pl.units * parts;
-    pl.grid2 = pl.max_parts > 0 ? static_cast<long long>(S) * pl.units * (D / 16) : 0;
     pl.records = static_cast<long long>(S) * pl.units * pl.max_parts;
+  }
+  if (!pl.balanced && pl.max_parts > 0) {
+    // phase 2 of fixed partitions: wide workgroups (fewer of them) when one round of
+    // loads covers a segment's partials, else one 16-wide slice per workgroup
+    const int per_round = pa::kRedThreads / (4 * balanced_slices(D)) * pa::reduce_unroll(pl.group);
+    pl.wide_reduce = pl.max_parts <= per_round;
+    pl.grid2 = static_cast<long long>(S) * pl.units *
+               (D / 16 / (pl.wide_reduce ? balanced_slices(D) : 1));
   }
   if (pl.grid1 > std::numeric_limits<int>::max() || pl.grid2 > std::numeric_limits<int>::max())
     return PA_ERR_SHAPE;
@@ -207,36 +265,35 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 // Phase 2 is instantiated per group size so its loads can all be in flight at once.
 template <int D, class DT, int G>
-void launch_reduce_g(bool balanced, unsigned grid, hipStream_t stream,
-                     const pa::DecodeArgs& args) {
-  if (balanced)
-    hipLaunchKernelGGL((pa::pa_reduce_kernel<D, DT, G, balanced_slices(D), true>), dim3(grid),
+void launch_reduce_g(bool wide, unsigned grid, hipStream_t stream, const pa::DecodeArgs& args) {
+  if (wide)
+    hipLaunchKernelGGL((pa::pa_reduce_kernel<D, DT, G, balanced_slices(D)>), dim3(grid),
                        dim3(pa::kRedThreads), 0, stream, args);
   else
-    hipLaunchKernelGGL((pa::pa_reduce_kernel<D, DT, G, 1, false>), dim3(grid),
-                       dim3(pa::kRedThreads), 0, stream, args);
+    hipLaunchKernelGGL((pa::pa_reduce_kernel<D, DT, G, 1>), dim3(grid), dim3(pa::kRedThreads), 0,
+                       stream, args);
 }
 
 template <int D, class DT>
-int launch_reduce(int group, bool balanced, unsigned grid, hipStream_t stream,
+int launch_reduce(int group, bool wide, unsigned grid, hipStream_t stream,
                   const pa::DecodeArgs& args) {
   switch (group) {
-    case 1: launch_reduce_g<D, DT, 1>(balanced, grid, stream, args); break;
-    case 2: launch_reduce_g<D, DT, 2>(balanced, grid, stream, args); break;
-    case 3: launch_reduce_g<D, DT, 3>(balanced, grid, stream, args); break;
-    case 4: launch_reduce_g<D, DT, 4>(balanced, grid, stream, args); break;
-    case 5: launch_reduce_g<D, DT, 5>(balanced, grid, stream, args); break;
-    case 6: launch_reduce_g<D, DT, 6>(balanced, grid, stream, args); break;
-    case 7: launch_reduce_g<D, DT, 7>(balanced, grid, stream, args); break;
-    case 8: launch_reduce_g<D, DT, 8>(balanced, grid, stream, args); break;
-    case 9: launch_reduce_g<D, DT, 9>(balanced, grid, stream, args); break;
-    case 10: launch_reduce_g<D, DT, 10>(balanced, grid, stream, args); break;
-    case 11: launch_reduce_g<D, DT, 11>(balanced, grid, stream, args); break;
-    case 12: launch_reduce_g<D, DT, 12>(balanced, grid, stream, args); break;
-    case 13: launch_reduce_g<D, DT, 13>(balanced, grid, stream, args); break;
-    case 14: launch_reduce_g<D, DT, 14>(balanced, grid, stream, args); break;
-    case 15: launch_reduce_g<D, DT, 15>(balanced, grid, stream, args); break;
-    case 16: launch_reduce_g<D, DT, 16>(balanced, grid, stream, args); break;
+    case 1: launch_reduce_g<D, DT, 1>(wide, grid, stream, args); break;
+    case 2: launch_reduce_g<D, DT, 2>(wide, grid, stream, args); break;
+    case 3: launch_reduce_g<D, DT, 3>(wide, grid, stream, args); break;
+    case 4: launch_reduce_g<D, DT, 4>(wide, grid, stream, args); break;
+    case 5: launch_reduce_g<D, DT, 5>(wide, grid, stream, args); break;
+    case 6: launch_reduce_g<D, DT, 6>(wide, grid, stream, args); break;
+    case 7: launch_reduce_g<D, DT, 7>(wide, grid, stream, args); break;
+    case 8: launch_reduce_g<D, DT, 8>(wide, grid, stream, args); break;
+    case 9: launch_reduce_g<D, DT, 9>(wide, grid, stream, args); break;
+    case 10: launch_reduce_g<D, DT, 10>(wide, grid, stream, args); break;
+    case 11: launch_reduce_g<D, DT, 11>(wide, grid, stream, args); break;
+    case 12: launch_reduce_g<D, DT, 12>(wide, grid, stream, args); break;
+    case 13: launch_reduce_g<D, DT, 13>(wide, grid, stream, args); break;
+    case 14: launch_reduce_g<D, DT, 14>(wide, grid, stream, args); break;
+    case 15: launch_reduce_g<D, DT, 15>(wide, grid, stream, args); break;
+    case 16: launch_reduce_g<D, DT, 16>(wide, grid, stream, args); break;
     default: return PA_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -248,7 +305,13 @@ int launch_decode(const pa::DecodeArgs& args, const Plan& pl, hipStream_t stream
   if (opt && opt->phase1_begin) {
     if (hipEventRecord(opt->phase1_begin, stream) != hipSuccess) return PA_ERR_HIP;
   }
-  if (pl.balanced)
+  if (pl.stream && pl.parts)
+    hipLaunchKernelGGL((pa::pa_phase1_stream_kernel<D, DT, kWaves, true>),
+                       dim3(static_cast<unsigned>(pl.grid1)), dim3(kWaves * 64), 0, stream, args);
+  else if (pl.stream)
+    hipLaunchKernelGGL((pa::pa_phase1_stream_kernel<D, DT, kWaves, false>),
+                       dim3(static_cast<unsigned>(pl.grid1)), dim3(kWaves * 64), 0, stream, args);
+  else if (pl.balanced)
     hipLaunchKernelGGL((pa::pa_phase1_balanced_kernel<D, DT, kWaves>),
                        dim3(static_cast<unsigned>(pl.grid1)), dim3(kWaves * 64), 0, stream, args);
   else
@@ -259,7 +322,7 @@ int launch_decode(const pa::DecodeArgs& args, const Plan& pl, hipStream_t stream
     if (hipEventRecord(opt->phase1_end, stream) != hipSuccess) return PA_ERR_HIP;
   }
   if (pl.grid2 > 0) {
-    const int st = launch_reduce<D, DT>(pl.group, pl.balanced, static_cast<unsigned>(pl.grid2),
+    const int st = launch_reduce<D, DT>(pl.group, pl.wide_reduce, static_cast<unsigned>(pl.grid2),
                                         stream, args);
     if (st != PA_OK) return st;
   }
@@ -305,6 +368,53 @@ PA_API size_t paged_attn_workspace_size(int num_seqs, int num_heads, int num_kv_
                                       max_blocks_per_seq, max_seq_len, partition_size, nullptr);
 }
 
+namespace {
+
+// Host mirror of the share boundaries of pa_phase1_stream_kernel with an explicit
+// partition size (plan information only): shares of the step's virtual tiles
+// (piece_cost per partition plus the real tiles), each boundary moved to the nearest
+// partition boundary; returns how many shares hold real tiles.
+long long stream_parts_busy_shares(const int32_t* lens, int S, const Plan& pl, int Hkv) {
+  const long long P16 = pl.P / 16, c = pl.piece_cost, unit = c + P16;
+  std::vector<long long> pre(S + 1, 0), preR(S + 1, 0);
+  std::vector<bool> single(S, false);
+  for (int s = 0; s < S; ++s) {
+    long long L = lens[s] < pl.max_seq_len ? lens[s] : pl.max_seq_len;
+    if (L < 0) L = 0;
+    const long long n = (L + 15) / 16;
+    single[s] = L <= pl.T1;
+    const long long np = n == 0 ? 0 : (single[s] ? 1 : (n + P16 - 1) / P16);
+    pre[s + 1] = pre[s] + np * c + n;
+    preR[s + 1] = preR[s] + n;
+  }
+  const long long T = pre[S], NS = pl.num_wg / Hkv;
+  auto seq_at = [&](long long x) {   // largest s < S with pre[s] <= x
+    int s = 0, top = S - 1;
+    while (s < top) {
+      const int mid = (s + top + 1) / 2;
+      if (pre[mid] <= x) s = mid; else top = mid - 1;
+    }
+    return s;
+  };
+  auto real_of_cut = [&](long long j) -> long long {
+    const long long x = pa::share_cut(T, j, NS, pl.xcd_skew);
+    if (x >= T) return preR[S];
+    const int s = seq_at(x);
+    const long long off = x - pre[s], cs = pre[s + 1] - pre[s], n = preR[s + 1] - preR[s];
+    if (single[s]) return preR[s] + (2 * off >= cs ? n : 0);
+    long long p = (2 * off + unit) / (2 * unit);
+    const long long np = (n + P16 - 1) / P16;
+    if (p > np) p = np;
+    return preR[s] + (p * P16 < n ? p * P16 : n);
+  };
+  long long busy = 0;
+  for (long long j = 0; j < NS; ++j)
+    if (real_of_cut(j) < real_of_cut(j + 1)) ++busy;
+  return busy;
+}
+
+}  // namespace
+
 PA_API int paged_attn_plan(const int32_t* seq_lens_host, int num_seqs, int num_heads,
                            int num_kv_heads, int head_dim, int block_size,
                            int max_blocks_per_seq, int max_seq_len, int partition_size,
@@ -331,6 +441,7 @@ PA_API int paged_attn_plan(const int32_t* seq_lens_host, int num_seqs, int num_h
   info->fused = pl.fused ? 1 : 0;
   info->xcd_skew = pl.xcd_skew;
   info->piece_cost = pl.piece_cost;
+  info->stream = pl.stream ? 1 : 0;
   if (seq_lens_host) {
     if (pl.balanced) {
       // host mirror of the device split: sequence s covers virtual tiles
@@ -369,6 +480,9 @@ PA_API int paged_attn_plan(const int32_t* seq_lens_host, int num_seqs, int num_h
                                      ((L + pl.P - 1) / pl.P);
         }
       }
+      if (pl.parts)
+        info->active_workgroups =
+            num_kv_heads * stream_parts_busy_shares(seq_lens_host, num_seqs, pl, num_kv_heads);
     }
   }
   return PA_OK;
@@ -559,6 +673,12 @@ PA_API int paged_attn_prefill(void* out, const void* q, const void* k_new, const
                        max_blocks_per_seq, max_ctx_len, 0, dtype);
   if (st != PA_OK) return st;
   if (!std::isfinite(scale) || max_query_len < 0 || max_ctx_len < 0) return PA_ERR_SHAPE;
+  // the kernel keeps the byte stride of a cache page (num_kv_heads rows of
+  // block_size x head_dim) and the byte offset of a 32-row step of the new keys in
+  // 32-bit registers
+  const unsigned long long row_block_bytes = static_cast<unsigned long long>(num_kv_heads) *
+                                             (block_size > 32 ? block_size : 32) * head_dim * 2;
+  if (row_block_bytes >= (1ULL << 32)) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0 || max_query_len == 0) return PA_OK;
   if (!out || !q || !k_new || !v_new || !key_cache || !value_cache || !block_tables ||
       !ctx_lens || !query_start)
@@ -606,6 +726,28 @@ PA_API int paged_attn_prefill(void* out, const void* q, const void* k_new, const
     default: f16 ? launch_prefill<64, pa::F16>(args, g, stream)
                  : launch_prefill<64, pa::BF16>(args, g, stream); break;
   }
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+PA_API int paged_attn_read_probe(const void* src, size_t chunk_bytes, const long long* order,
+                                 long long num_chunks, int num_workgroups, unsigned* sink,
+                                 hipStream_t stream) {
+  if (chunk_bytes != 4096 && chunk_bytes != 8192 && chunk_bytes != 16384) return PA_ERR_UNSUPPORTED;
+  if (num_chunks < 0 || num_workgroups < 1 || num_workgroups > (1 << 20)) return PA_ERR_SHAPE;
+  if (num_chunks == 0) return PA_OK;
+  if (!src || !sink) return PA_ERR_NULL;
+  if (!aligned(src, 16) || !aligned(sink, 4) || (order && !aligned(order, 8))) return PA_ERR_ALIGN;
+  const auto* s = static_cast<const pa::u32x4*>(src);
+  const dim3 grid(static_cast<unsigned>(num_workgroups));
+  if (chunk_bytes == 4096)
+    hipLaunchKernelGGL(pa::pa_read_probe_kernel<4096>, grid, dim3(256), 0, stream, s, order,
+                       num_chunks, sink);
+  else if (chunk_bytes == 8192)
+    hipLaunchKernelGGL(pa::pa_read_probe_kernel<8192>, grid, dim3(256), 0, stream, s, order,
+                       num_chunks, sink);
+  else
+    hipLaunchKernelGGL(pa::pa_read_probe_kernel<16384>, grid, dim3(256), 0, stream, s, order,
+                       num_chunks, sink);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -143,6 +143,18 @@ typedef struct pa_options {
      * immediately before/after the phase-1 kernel (instrumentation only). */
     hipEvent_t phase1_begin;
     hipEvent_t phase1_end;
+    /* Phase-1 walk for explicit partition sizes and the length-balanced split.
+     * 0 (default): per-wave streams where supported (up to 1024 sequences, not with
+     * the fused combine or the per-query-head ablation): every wave of a workgroup
+     * streams its own contiguous run of tiles across pieces, finishing a piece
+     * that lies inside it from registers, and only pieces cut between waves are
+     * merged, once, at the end;
+     * with an explicit partition size, shares end on partition boundaries so each
+     * partition still yields one partial.  Negative:
+     * one workgroup per piece with a merge of its waves after every piece (the
+     * pages' dense (sequence, KV head, partition) grid for explicit partition
+     * sizes). */
+    int stream_walk;
 } pa_options;
 
 /* What a call will launch; filled by paged_attn_plan. */
@@ -163,11 +175,20 @@ typedef struct pa_plan_info {
     int fused;                 /* 1: partials merged in phase 1, no phase-2 launch */
     int xcd_skew;              /* XCD-paired shares in use (permille), 0 = equal */
     int piece_cost;            /* balanced split: tiles a piece start counts as */
+    int stream;                /* 1: phase 1 walks per-wave streams (pa_options.stream_walk) */
 } pa_plan_info;
 
 /*
  * Bytes of device workspace paged_attn_decode needs for these sizes (0 when every
- * sequence can run in a single pass).  max_seq_len <= 0 means "unknown", and the
+ * sequence can run in a single pass).  The pages keep the decode's buffers
+ * preallocated and reuse them across calls so the hot call allocates nothing
+ * (page of commit b80fd2b, paged_attn.py, the caching-allocator passage); here the
+ * caller owns that buffer, sized by this call.  What it holds is the phase-1
+ * compound partial of the page of commit 8d26e23 (attention_partial: max_score,
+ * exp_sum, weighted_v).  Besides the sizes of the spec call it takes
+ * num_kv_heads (the grid is on KV heads, so the partial count depends on it),
+ * block_size and max_blocks_per_seq (the table capacity bounds the length when
+ * max_seq_len <= 0, and the automatic split depends on the page size).  max_seq_len <= 0 means "unknown", and the
  * table capacity max_blocks_per_seq*block_size is used.  Returns (size_t)-1 for
  * arguments paged_attn_decode would reject.
  *
@@ -188,7 +209,12 @@ size_t paged_attn_workspace_size_ex(int num_seqs, int num_heads, int num_kv_head
 
 /*
  * Decode attention for one step of a batch (the whole hot path: phase 1 with the
- * length-tiered dispatch, then phase 2 for partitioned sequences).
+ * length-tiered dispatch, then phase 2 for partitioned sequences).  Page of commit
+ * 8d26e23: the grid on KV heads ("Key design change"), the phase-1 kernel writing
+ * one attention_partial per (sequence, KV head, partition) for the group's query
+ * heads, the phase-2 kernel merging them with the flash-attention rescale; page of
+ * commit 87a19d2: that rescale (the online-softmax fix); page of commit b80fd2b:
+ * the length-tiered dispatch (three-tier decode dispatch).
  *
  *   out                 [num_seqs][num_heads][head_dim] dtype, written (device)
  *   q                   [num_seqs][num_heads][head_dim] dtype (device)
@@ -231,7 +257,9 @@ int paged_attn_decode(void* out, const void* q, const void* key_cache, const voi
                       int max_blocks_per_seq, int max_seq_len, int dtype,
                       size_t workspace_bytes);
 
-/* paged_attn_decode with tuning/instrumentation options (opt may be NULL). */
+/* paged_attn_decode with tuning/instrumentation options (opt may be NULL): the
+ * tier threshold and partition choices the page of commit 8d26e23 says should be
+ * tunable, the in-kernel combine (its level 3), and the ablation of its grid. */
 int paged_attn_decode_ex(void* out, const void* q, const void* key_cache,
                          const void* value_cache, const int32_t* block_tables,
                          const int32_t* seq_lens, int num_seqs, int num_heads,
@@ -300,6 +328,8 @@ int paged_attn_decode_noalloc(void* out, const void* q, const void* key_cache,
                               int max_seq_len, int dtype);
 
 /*
+ * Workspace set-up for the in-kernel cross-partition combine (the level-3 combine
+ * of the three-level decomposition, page of commit 8d26e23).
  * Clears the ticket area (the first min(workspace_bytes,
  * PA_WORKSPACE_TICKET_BYTES) bytes) of a workspace with a kernel on `stream`, as
  * the fused combine (pa_options.fused_combine) needs before the first call on a
@@ -309,11 +339,15 @@ int paged_attn_decode_noalloc(void* out, const void* q, const void* key_cache,
  */
 int paged_attn_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Human-readable text for a pa_status_t (static storage, never NULL). */
+/* Human-readable text for a pa_status_t (static storage, never NULL).  Errors are
+ * returned, never served by a fallback path (the try/except fallbacks of the page
+ * of commit b80fd2b are what this interface does not do). */
 const char* paged_attn_status_str(int status);
 
 /*
- * Host-only planning (no HIP call, usable without a GPU): fills *info with the
+ * Host-only planning (no HIP call, usable without a GPU), the length-tiered
+ * dispatch of the page of commit b80fd2b (three-tier decode dispatch) and the grid
+ * of the page of commit 8d26e23 ((sequence, KV head, partition)): fills *info with the
  * grid, tier threshold, partition size and workspace a decode call with the same
  * arguments would use.  seq_lens_host (host pointer, may be NULL) adds the
  * per-sequence tier counts and the number of phase-1 workgroups that do work.
@@ -327,7 +361,8 @@ int paged_attn_plan(const int32_t* seq_lens_host, int num_seqs, int num_heads,
 
 /*
  * Test hook for the block-table gather (the addressing and 16-byte page loads of
- * phase 1, without the attention math): writes the K and V rows of tokens
+ * phase 1, without the attention math), the gather of K/V by block id of the page
+ * of commit b80fd2b (paged_attn.py, rewrite item 1): writes the K and V rows of tokens
  * t < seq_lens[s] to k_out/v_out, laid out [num_seqs][num_kv_heads][max_seq_len]
  * [head_dim] (16-bit elements copied bit for bit; other slots are not written).
  * max_seq_len must be > 0 and <= max_blocks_per_seq*block_size.
@@ -337,6 +372,27 @@ int paged_attn_gather_probe(void* k_out, void* v_out, const void* key_cache,
                             const int32_t* seq_lens, int num_seqs, int num_kv_heads,
                             int head_dim, int block_size, int max_blocks_per_seq,
                             int max_seq_len, hipStream_t stream);
+
+/*
+ * Measurement hook: the read bandwidth the decode is bounded by.  The pages' case
+ * for the KV-head grid is the K/V bytes read (page of commit 8d26e23, "Key design
+ * change": 6x fewer), so the decode's roofline is HBM read bandwidth; this call
+ * measures what the device delivers to the same access pattern (the phase-1 load
+ * form: nontemporal 16-byte loads, 1 KiB contiguous per instruction, two chunks in
+ * flight per wave).  It reads num_chunks chunks of chunk_bytes bytes (4096, 8192
+ * or 16384: one (page, KV head) block of the caches) from src, chunk i at
+ * src + order[i] * chunk_bytes, or at src + i * chunk_bytes when order is NULL,
+ * spread over num_workgroups workgroups of 256 threads, and writes one XOR fold
+ * per workgroup to sink[num_workgroups] (so no load is dead).
+ *   src    device, 16-byte aligned, at least (max index + 1) * chunk_bytes bytes
+ *   order  device int64 [num_chunks] or NULL; every entry must index a chunk of src
+ *          (not checked: an entry outside src faults the device)
+ * Returns PA_OK, PA_ERR_UNSUPPORTED (chunk size), PA_ERR_SHAPE, PA_ERR_NULL,
+ * PA_ERR_ALIGN or PA_ERR_HIP.
+ */
+int paged_attn_read_probe(const void* src, size_t chunk_bytes, const long long* order,
+                          long long num_chunks, int num_workgroups, unsigned* sink,
+                          hipStream_t stream);
 
 #ifdef __cplusplus
 }

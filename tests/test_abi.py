@@ -106,25 +106,39 @@ def test_workspace_size_formula(lib):
 
 def test_plan_matches_pages_grid(lib):
     """One 100K-token sequence with 512-token partitions: 200 partitions and a grid
-    of 4 KV heads x 200 = 800 workgroups instead of 24 x 200 = 4800."""
+    of 4 KV heads x 200 = 800 workgroups instead of 24 x 200 = 4800 (the dense grid,
+    stream_walk -1).  The default walks the same 800 partitions, one partial each,
+    with per-wave streams on one workgroup per CU."""
     g = golden()
     L, P = g["long_seq_tokens"], g["partition_size"]
-    info = pa.plan([L], g["num_q_heads"], g["num_kv_heads"], g["tile_head_dim"], 16,
-                   L // 16, L, P, single_pass_max_len=0)
+    args = ([L], g["num_q_heads"], g["num_kv_heads"], g["tile_head_dim"], 16, L // 16, L, P)
+    info = pa.plan(*args, single_pass_max_len=0, stream_walk=-1)
+    assert info["stream"] == 0
     assert info["max_partitions"] == g["num_partitions"]
     assert info["phase1_workgroups"] == g["blocks_per_kv_head_grid"]
     assert info["phase1_workgroups"] * info["group"] == g["blocks_per_q_head_grid"]
     assert info["group"] == g["gqa_ratio"] == g["kv_reads_saved_factor"]
     assert info["active_workgroups"] == 800
     assert info["partitioned_seqs"] == 1
+    # per-wave streams: the same partitions and partial records, 64 shares x 4 KV heads
+    st = pa.plan(*args, single_pass_max_len=0)
+    assert st["stream"] == 1 and st["max_partitions"] == g["num_partitions"]
+    assert st["phase1_workgroups"] == 256 and st["active_workgroups"] == 256
+    assert st["workspace_bytes"] == info["workspace_bytes"]
+    assert st["phase2_workgroups"] == info["phase2_workgroups"] == 4 * 16
     # the per-query-head ablation restores the pages' "before" grid
-    info_q = pa.plan([L], g["num_q_heads"], g["num_kv_heads"], g["tile_head_dim"], 16,
-                     L // 16, L, P, single_pass_max_len=0, per_query_head=True)
-    assert info_q["phase1_workgroups"] == g["blocks_per_q_head_grid"]
+    info_q = pa.plan(*args, single_pass_max_len=0, per_query_head=True)
+    assert info_q["phase1_workgroups"] == g["blocks_per_q_head_grid"] and info_q["stream"] == 0
     assert info_q["group"] == 1 and info_q["workspace_bytes"] == info["workspace_bytes"]
     # the same arithmetic for the 4-sequence long-context workload
-    info4 = pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, P)
+    info4 = pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, P, stream_walk=-1)
     assert info4["phase1_workgroups"] == 3200 and info4["phase2_workgroups"] == 4 * 4 * 16
+    st4 = pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, P)
+    assert st4["phase1_workgroups"] == 256 and st4["phase2_workgroups"] == 4 * 4 * 16
+    assert st4["xcd_skew"] == 80                # shares (whole partitions) paired by XCD
+    # a partition per share at most: 3 sequences of 2 partitions -> 6 shares per KV head
+    few = pa.plan([1024] * 3, 24, 4, 256, 16, 64, 1024, 512, single_pass_max_len=0)
+    assert few["phase1_workgroups"] == 4 * 6 and few["active_workgroups"] == 4 * 6
 
 
 def test_tier_thresholds(lib):
@@ -136,10 +150,13 @@ def test_tier_thresholds(lib):
     assert info["single_pass_max_len"] == g["single_pass_max_len"]
     assert info["single_pass_seqs"] == 256 and info["partitioned_seqs"] == 8
     # automatic tier: a sequence that fits in one partition runs in one pass
-    info = pa.plan([512, 513, 8192], 24, 4, 256, 16, 512, 0, 512)
+    info = pa.plan([512, 513, 8192], 24, 4, 256, 16, 512, 0, 512, stream_walk=-1)
     assert info["single_pass_max_len"] == 512
     assert info["single_pass_seqs"] == 1 and info["partitioned_seqs"] == 2
     assert info["active_workgroups"] == 4 * (1 + 2 + 16)
+    st = pa.plan([512, 513, 8192], 24, 4, 256, 16, 512, 0, 512)
+    assert st["stream"] == 1 and st["single_pass_seqs"] == 1 and st["partitioned_seqs"] == 2
+    assert st["active_workgroups"] == 4 * (1 + 2 + 16)     # 19 pieces, 64 shares
     # explicit partition sizes
     for P in (256, 512, 1024):
         info = pa.plan([65536], 24, 4, 256, 16, 4096, 65536, P, single_pass_max_len=8192)
@@ -158,7 +175,9 @@ def test_balanced_split_plan(lib):
     assert info["active_workgroups"] == 256 and info["partitioned_seqs"] == 4
     assert info["phase2_workgroups"] == 256 * 2
     assert pa.plan([L] * 4, 24, 4, 128, 16, L // 16, L, 0)["phase1_workgroups"] == 512
-    assert pa.plan([L] * 4, 24, 4, 256, 8, L // 8, L, 0)["phase1_workgroups"] == 512
+    assert pa.plan([L] * 4, 24, 4, 256, 8, L // 8, L, 0, stream_walk=-1)["phase1_workgroups"] == 512
+    # per-wave streams at head_dim 256 take 126 KiB of LDS: one workgroup per CU
+    assert pa.plan([L] * 4, 24, 4, 256, 8, L // 8, L, 0)["phase1_workgroups"] == 256
     # 1024 segments of 1024 tiles over 256 workgroups: equal shares end on segment ends
     info = pa.plan([16384] * 256, 24, 4, 256, 32, 512, 16384, 0, xcd_skew=-1)
     assert info["phase1_workgroups"] == 256 and info["xcd_skew"] == 0
@@ -250,9 +269,11 @@ def test_fused_combine_plan(lib):
     """The fused combine drops the phase-2 launch and keeps the workspace layout;
     it is declined when the ticket area cannot hold one counter per segment."""
     L, P = 102400, 512
-    base = pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, P)
+    base = pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, P, stream_walk=-1)
     fused = pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, P, fused_combine=True)
     assert base["fused"] == 0 and base["phase2_workgroups"] == 4 * 4 * 16
+    # the fused combine runs on one workgroup per piece (no per-wave streams)
+    assert fused["stream"] == 0 and pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, P)["stream"] == 1
     assert fused["fused"] == 1 and fused["phase2_workgroups"] == 0
     assert fused["phase1_workgroups"] == base["phase1_workgroups"]
     assert fused["workspace_bytes"] == base["workspace_bytes"]
@@ -302,11 +323,31 @@ def test_prefill_validation_errors_before_any_launch(lib):
     assert prefill_call(lib, out=ctypes.c_void_p(0x10004)) == 7
     assert prefill_call(lib, S=0) == 0                      # nothing to do
     assert prefill_call(lib, mq=0) == 0
+    # a cache page of 64 KV heads x 131072 slots x 256 dims is 2^32 bytes: its stride
+    # does not fit the kernel's 32-bit page offsets, so the shape is refused
+    assert prefill_call(lib, Hq=64, Hkv=64, bs=131072, mbps=1, mc=1024) == 3
+    assert prefill_call(lib, Hq=64, Hkv=32, bs=131072, mbps=1, mc=1024, S=0) == 0
+
+
+def test_read_probe_validation(lib):
+    """The read probe rejects what it cannot run before any launch."""
+    sink = FAKE
+    P, L = ctypes.c_void_p, ctypes.c_longlong
+    assert lib.paged_attn_read_probe(FAKE, 1000, None, L(4), 256, sink, None) == 3
+    assert lib.paged_attn_read_probe(FAKE, 8192, None, L(4), 0, sink, None) == 2
+    assert lib.paged_attn_read_probe(FAKE, 8192, None, L(-1), 256, sink, None) == 2
+    assert lib.paged_attn_read_probe(None, 8192, None, L(4), 256, sink, None) == 1
+    assert lib.paged_attn_read_probe(FAKE, 8192, None, L(4), 256, None, None) == 1
+    assert lib.paged_attn_read_probe(P(0x10008), 8192, None, L(4), 256, sink, None) == 7
+    assert lib.paged_attn_read_probe(FAKE, 8192, P(0x10004), L(4), 256, sink, None) == 7
+    assert lib.paged_attn_read_probe(None, 8192, None, L(0), 256, None, None) == 0
 
 
 def test_xcd_paired_shares_plan(lib):
     """Automatic splits pair their shares across XCD parities (default 80 permille);
-    explicit partition sizes and the per-query-head ablation keep equal ones."""
+    so do the shares of whole partitions that per-wave streams walk with an explicit
+    partition size, while the pages' dense grid and the per-query-head ablation keep
+    equal work per workgroup."""
     L = 102400
     hinted = pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0, total_tokens_hint=4 * L)
     assert hinted["balanced"] == 0 and hinted["max_partitions"] == 16
@@ -317,7 +358,8 @@ def test_xcd_paired_shares_plan(lib):
                    xcd_skew=-1)["xcd_skew"] == 0
     assert pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0, total_tokens_hint=4 * L,
                    xcd_skew=900)["xcd_skew"] == 500
-    assert pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 512)["xcd_skew"] == 0
+    assert pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 512, stream_walk=-1)["xcd_skew"] == 0
+    assert pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 512)["xcd_skew"] == 80
     assert pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0, total_tokens_hint=4 * L,
                    per_query_head=True)["xcd_skew"] == 0
     assert pa.plan([L] * 4, 24, 4, 256, 16, L // 16, L, 0)["xcd_skew"] == 80

@@ -163,26 +163,32 @@ BALANCED = {
 }
 
 
+@pytest.mark.parametrize("walk", [0, -1], ids=["streams", "piece-per-workgroup"])
 @pytest.mark.parametrize("bs,dtype", [(8, "bf16"), (16, "f16"), (32, "bf16")])
-def test_needles_every_tile_mixed_lengths(bs, dtype):
-    say(f"case needles mixed lengths bs={bs} {dtype}")
+def test_needles_every_tile_mixed_lengths(bs, dtype, walk):
+    """walk 0: per-wave streams (wave ranges, pieces cut between waves and merged,
+    partitions kept whole per share); -1: one workgroup per piece."""
+    say(f"case needles mixed lengths bs={bs} {dtype} walk={walk}")
     pool = NeedlePool(MIXED, bs, dtype, seed=bs)
     lens = list(pool.lens)
     for name, kw in BALANCED.items():
         info = pa.plan(lens, HQ, HKV, D, bs, pool.bt_host.shape[1], pool.max_len, 0,
                        xcd_skew=kw["xcd_skew"], piece_cost=kw["piece_cost"],
-                       fused_combine=kw.get("fused_combine", False))
+                       fused_combine=kw.get("fused_combine", False), stream_walk=walk)
         assert info["balanced"] == 1 and info["partitioned_seqs"] >= 6, info
         say(f"  balanced {name}: {info['phase1_workgroups']} workgroups, "
-            f"{info['partitioned_seqs']} sequences cut")
+            f"{info['partitioned_seqs']} sequences cut, streams {info['stream']}")
         for c in range(pool.calls()):
-            pool.check(c, f"bs{bs}/balanced/{name}", partition_size=0, **kw)
+            pool.check(c, f"bs{bs}/balanced/{name}/walk{walk}", partition_size=0,
+                       stream_walk=walk, **kw)
     for name, kw in {"p512": dict(partition_size=512, single_pass_max_len=0),
+                     "p64": dict(partition_size=64, single_pass_max_len=0),
+                     "p512-auto-tier": dict(partition_size=512),
                      "single-pass": dict(partition_size=512, single_pass_max_len=ALL_SINGLE)
                      }.items():
         say(f"  {name}")
         for c in range(pool.calls()):
-            pool.check(c, f"bs{bs}/{name}", **kw)
+            pool.check(c, f"bs{bs}/{name}/walk{walk}", stream_walk=walk, **kw)
     del pool
     torch.cuda.empty_cache()
 

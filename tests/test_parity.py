@@ -289,7 +289,8 @@ def test_needle_high_page_ids():
 @pytest.mark.parametrize("P", [256, 1024, 0])
 def test_per_query_head_ablation(P):
     """One workgroup per query head computes each head's column exactly as the
-    grouped workgroup does: with the same partitions the outputs agree bit for bit.
+    grouped workgroup of the same dense grid does (one workgroup per piece,
+    stream_walk -1): with the same partitions the outputs agree bit for bit.
     (P = 0 sizes partitions per head unit, so only the oracle check applies.)"""
     say(f"case per-query-head ablation P={P}")
     w = make([1, 100, 700, 2000], partition_size=256)
@@ -297,7 +298,7 @@ def test_per_query_head_ablation(P):
                          partition_size=P, max_seq_len=w.max_seq_len, single_pass_max_len=0,
                          per_query_head=True)
     if P:
-        grouped = run(w, 0, P=P)
+        grouped = run(w, 0, P=P, stream_walk=-1)
         torch.cuda.synchronize()
         assert torch.equal(grouped, ablation)
     assert_close(gpu_out(ablation), oracle_full(w), "per-query-head")
