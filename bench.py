@@ -86,11 +86,47 @@ def traffic_from_counters(units_bytes):
 def default_command(args) -> bool:
     """True when the run is the configuration the committed counters were taken on
     (the long workload with automatic partitions and the host-side length total)."""
-    return (args.workload == "long" and args.partition_size == 0 and not args.p512
+    return (args.workload == "long" and args.partition_size == 0
             and args.single_pass_max_len is None and not args.per_query_head
             and not args.fused and not args.no_hint and args.num_cus == 0
             and args.head_dim == 256 and args.block_size == 16 and args.xcd_skew == 0
             and args.piece_cost == 0)
+
+
+def read_ceiling(torch, pa, dev, w, gib: int = 4, reps: int = 10):
+    """Read bandwidth the device delivers to phase 1's access pattern (the library's
+    read probe): `gib` GiB read in order, and the same bytes as chunks of one
+    (page, KV head) block each (block_size x head_dim x 2 bytes) in a random order,
+    256 workgroups as in phase 1; median of `reps` timed launches each."""
+    chunk = w.block_size * w.head_dim * 2
+    if chunk not in (4096, 8192, 16384):
+        return None
+    n = (gib << 30) // chunk
+    src = torch.empty(n * chunk, dtype=torch.uint8, device=dev).fill_(7)
+    g = torch.Generator(device=dev).manual_seed(5)
+    order = torch.randperm(n, generator=g, device=dev)
+    sink = torch.empty(256, dtype=torch.int32, device=dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    for name, o in (("contiguous_gbs", None), ("gather_gbs", order)):
+        for _ in range(2):
+            pa.read_probe(src, chunk, o, sink=sink)
+        ms = []
+        for _ in range(reps):
+            start.record()
+            pa.read_probe(src, chunk, o, sink=sink)
+            stop.record()
+            torch.cuda.synchronize()
+            ms.append(start.elapsed_time(stop))
+        res[name] = round(n * chunk / (sorted(ms)[reps // 2] * 1e-3) / 1e9, 1)
+    del src, order
+    torch.cuda.empty_cache()
+    res.update({"bytes": n * chunk, "chunk_bytes": chunk, "workgroups": 256,
+                "kernel": "pa_read_probe_kernel (nontemporal 16-byte loads, 1 KiB per "
+                          "instruction, two chunks in flight per wave)"})
+    log(f"read ceiling: contiguous {res['contiguous_gbs']} GB/s, "
+        f"{chunk}-byte chunks shuffled {res['gather_gbs']} GB/s")
+    return res
 
 
 def cpu_baseline(w, nseqs: int):
@@ -199,8 +235,11 @@ def main():
                     choices=["tiny", "batch", "long", "mixed", "saturation", "prefill"])
     ap.add_argument("--partition-size", type=int, default=0,
                     help="tokens per partition; 0 = automatic (one workgroup per CU)")
-    ap.add_argument("--p512", action="store_true",
-                    help="also time the pages' fixed 512-token partitions (context only)")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the context timings (the plain call without the host-side "
+                         "length total, the pages' explicit partition sizes)")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip the read-ceiling measurement")
     ap.add_argument("--single-pass-max-len", type=int, default=None)
     ap.add_argument("--per-query-head", action="store_true",
                     help="ablation: one workgroup per query head (KV read once per query head)")
@@ -260,11 +299,12 @@ def main():
         w = workloads.NAMED[args.workload](device="cuda")
     torch.cuda.synchronize()
 
-    def decoder(P):
+    def decoder(P, hint=None):
         return pa.Decoder(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size,
                           w.max_blocks_per_seq, w.q.dtype, max_seq_len=w.max_seq_len,
                           partition_size=P, single_pass_max_len=args.single_pass_max_len,
-                          num_cus=args.num_cus, total_tokens_hint=total,
+                          num_cus=args.num_cus,
+                          total_tokens_hint=total if hint is None else hint,
                           per_query_head=args.per_query_head, fused_combine=args.fused,
                           xcd_skew=args.xcd_skew, piece_cost=args.piece_cost)
 
@@ -346,15 +386,27 @@ def main():
     del flush
     cold_ms = sorted(cold)[len(cold) // 2]
     log(f"cold: median {cold_ms * 1e3:.1f} us/step over {len(cold)} steps")
-    # context: the pages' fixed 512-token partitions on the same inputs
-    p512_ms = None
-    if P != 512 and args.p512:
-        d512 = decoder(512)
+    # context on the same inputs: the plain call (paged_attn_decode's defaults: no
+    # host-side length total, so partition_size 0 is the length-balanced split) and
+    # the pages' explicit partition sizes
+    variants = {}
+    if not args.no_variants:
+        if total and P == 0:
+            variants["plain_call"] = dict(P=0, hint=0)
+        sweep = [256, 512, 1024] if args.workload == "mixed" else [512]
+        for p in sweep:
+            if p != P:
+                variants[f"partition_{p}"] = dict(P=p, hint=total)
+    variant_us = {}
+    for name, v in variants.items():
+        d = decoder(v["P"], v["hint"])
         for _ in range(args.warmup):
-            step(d512)
-        p512_ms, _ = timed(d512, args.steps)
-        log(f"partition_size=512: {p512_ms * 1e3:.1f} us/step")
-        del d512
+            step(d)
+        ms, _ = timed(d, args.steps)
+        variant_us[name] = round(ms * 1e3, 2)
+        log(f"{name}: {ms * 1e3:.1f} us/step ({w.kv_bytes / (ms * 1e-3) / 1e9:.0f} GB/s)")
+        del d
+    ceiling = None if args.no_read_probe else read_ceiling(torch, pa, dev, w)
 
     # algorithmic bytes: one unit = one (token, KV head); it reads a K row and a V row
     units = int(w.seq_lens_host.clip(0).astype("int64").sum()) * w.num_kv_heads
@@ -380,7 +432,8 @@ def main():
         "us_per_step_hot": round(step_ms * 1e3, 2),
         "us_per_step_cold": round(cold_ms * 1e3, 2),
         "pct_hbm_peak": round(100 * eff / HBM_PEAK_GBS, 2),
-        "us_per_step_partition_512": None if p512_ms is None else round(p512_ms * 1e3, 2),
+        "us_per_step_variants": variant_us,
+        "read_ceiling": ceiling,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -409,7 +462,9 @@ def main():
                      "traffic": traffic_from_counters(kv) if default_command(args) else None,
                      "algorithmic_bytes_per_launch": kv, "bytes_per_unit": bytes_per_unit,
                      "units_per_launch": units,
-                     "avg_launch_us": round(ph1_avg * 1e3, 2)},
+                     "avg_launch_us": round(ph1_avg * 1e3, 2),
+                     "frac_of_read_ceiling": None if not ceiling else
+                     round(achieved / ceiling["gather_gbs"], 4)},
     }
     if not args.no_cpu:
         log(f"timing the CPU oracle on {min(args.cpu_seqs, w.num_seqs)} sequences")
