@@ -90,7 +90,7 @@ def default_command(args) -> bool:
             and args.single_pass_max_len is None and not args.per_query_head
             and not args.fused and not args.no_hint and args.num_cus == 0
             and args.head_dim == 256 and args.block_size == 16 and args.xcd_skew == 0
-            and args.piece_cost == 0)
+            and args.piece_cost == 0 and args.stream_walk == 0 and not args.head_sequential)
 
 
 def read_ceiling(torch, pa, dev, w, gib: int = 4, reps: int = 10):
@@ -243,6 +243,10 @@ def main():
     ap.add_argument("--single-pass-max-len", type=int, default=None)
     ap.add_argument("--per-query-head", action="store_true",
                     help="ablation: one workgroup per query head (KV read once per query head)")
+    ap.add_argument("--head-sequential", action="store_true",
+                    help="ablation: the group's query heads taken one after another per tile")
+    ap.add_argument("--stream-walk", type=int, default=0,
+                    help="-1: one workgroup per piece instead of per-wave streams")
     ap.add_argument("--fused", action="store_true",
                     help="merge partitions inside phase 1 (atomic ticket) instead of a phase-2 launch")
     ap.add_argument("--head-dim", type=int, default=256,
@@ -306,7 +310,8 @@ def main():
                           num_cus=args.num_cus,
                           total_tokens_hint=total if hint is None else hint,
                           per_query_head=args.per_query_head, fused_combine=args.fused,
-                          xcd_skew=args.xcd_skew, piece_cost=args.piece_cost)
+                          xcd_skew=args.xcd_skew, piece_cost=args.piece_cost,
+                          stream_walk=args.stream_walk, head_sequential=args.head_sequential)
 
     P = args.partition_size
     # the caller knows its sequence lengths on the host: pass their sum
@@ -317,7 +322,8 @@ def main():
                    single_pass_max_len=args.single_pass_max_len, num_cus=args.num_cus,
                    total_tokens_hint=total, per_query_head=args.per_query_head,
                    fused_combine=args.fused, xcd_skew=args.xcd_skew,
-                   piece_cost=args.piece_cost)
+                   piece_cost=args.piece_cost, stream_walk=args.stream_walk,
+                   head_sequential=args.head_sequential)
     log(f"plan: {info}")
 
     if args.copy_probe_mib > 0:
@@ -450,12 +456,16 @@ def main():
                    "split": "balanced" if info["balanced"] else "fixed partitions",
                    "xcd_skew_permille": info["xcd_skew"],
                    "piece_cost_tiles": info["piece_cost"] if info["balanced"] else None,
-                   "grid": "per query head (ablation)" if args.per_query_head else "per KV head",
+                   "grid": "per query head (ablation)" if args.per_query_head else
+                   ("per KV head, heads in turn (ablation)" if args.head_sequential
+                    else "per KV head"),
+                   "walk": "per-wave streams" if info["stream"] else "workgroup per piece",
                    "combine": "fused in phase 1" if info["fused"] else
                    ("phase-2 kernel" if info["phase2_workgroups"] else "none (one pass)"),
                    "kv_bytes_per_step": kv, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm",
-                     "kernel": "pa_phase1_balanced_kernel" if info["balanced"] else "pa_phase1_kernel",
+                     "kernel": "pa_phase1_stream_kernel" if info["stream"] else
+                     ("pa_phase1_balanced_kernel" if info["balanced"] else "pa_phase1_kernel"),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      # the committed counters cover the default command only

@@ -30,7 +30,7 @@ class Options(ctypes.Structure):
                 ("fused_combine", ctypes.c_int), ("xcd_skew", ctypes.c_int),
                 ("piece_cost", ctypes.c_int),
                 ("phase1_begin", ctypes.c_void_p), ("phase1_end", ctypes.c_void_p),
-                ("stream_walk", ctypes.c_int)]
+                ("stream_walk", ctypes.c_int), ("head_sequential", ctypes.c_int)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -43,7 +43,7 @@ class PlanInfo(ctypes.Structure):
                 ("threads_per_workgroup", ctypes.c_int), ("lds_bytes_phase1", ctypes.c_int),
                 ("balanced", ctypes.c_int), ("fused", ctypes.c_int),
                 ("xcd_skew", ctypes.c_int), ("piece_cost", ctypes.c_int),
-                ("stream", ctypes.c_int)]
+                ("stream", ctypes.c_int), ("head_sequential", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -104,9 +104,11 @@ def _check(status: int):
 def _opts(single_pass_max_len: Optional[int], num_cus: int = 0,
           events: Optional[Tuple[int, int]] = None, total_tokens_hint: int = 0,
           per_query_head: bool = False, fused_combine: bool = False,
-          xcd_skew: int = 0, piece_cost: int = 0, stream_walk: int = 0) -> Options:
+          xcd_skew: int = 0, piece_cost: int = 0, stream_walk: int = 0,
+          head_sequential: bool = False) -> Options:
     o = Options()
     o.stream_walk = int(stream_walk)
+    o.head_sequential = 1 if head_sequential else 0
     o.xcd_skew = int(xcd_skew)
     o.piece_cost = int(piece_cost)
     o.per_query_head = 1 if per_query_head else 0
@@ -128,7 +130,8 @@ def plan(seq_lens_host, num_heads: int, num_kv_heads: int, head_dim: int, block_
          dtype: int = PA_F16, single_pass_max_len: Optional[int] = None,
          num_seqs: Optional[int] = None, num_cus: int = 0, total_tokens_hint: int = 0,
          per_query_head: bool = False, fused_combine: bool = False,
-         xcd_skew: int = 0, piece_cost: int = 0, stream_walk: int = 0) -> dict:
+         xcd_skew: int = 0, piece_cost: int = 0, stream_walk: int = 0,
+         head_sequential: bool = False) -> dict:
     """Host-only plan (no GPU needed).  seq_lens_host: sequence of ints or None."""
     arr = None
     if seq_lens_host is not None:
@@ -138,7 +141,7 @@ def plan(seq_lens_host, num_heads: int, num_kv_heads: int, head_dim: int, block_
     info = PlanInfo()
     o = _opts(single_pass_max_len, num_cus, total_tokens_hint=total_tokens_hint,
               per_query_head=per_query_head, fused_combine=fused_combine, xcd_skew=xcd_skew,
-              piece_cost=piece_cost, stream_walk=stream_walk)
+              piece_cost=piece_cost, stream_walk=stream_walk, head_sequential=head_sequential)
     _check(lib().paged_attn_plan(arr, int(num_seqs or 0), num_heads, num_kv_heads, head_dim,
                                  block_size, max_blocks_per_seq, max_seq_len, partition_size,
                                  dtype, ctypes.byref(o), ctypes.byref(info)))
@@ -150,10 +153,10 @@ def workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: i
                    partition_size: int = 0, single_pass_max_len: Optional[int] = None,
                    total_tokens_hint: int = 0, num_cus: int = 0,
                    per_query_head: bool = False, stream_walk: int = 0,
-                   fused_combine: bool = False) -> int:
+                   fused_combine: bool = False, head_sequential: bool = False) -> int:
     o = _opts(single_pass_max_len, num_cus, total_tokens_hint=total_tokens_hint,
               per_query_head=per_query_head, stream_walk=stream_walk,
-              fused_combine=fused_combine)
+              fused_combine=fused_combine, head_sequential=head_sequential)
     n = lib().paged_attn_workspace_size_ex(num_seqs, num_heads, num_kv_heads, head_dim,
                                            block_size, max_blocks_per_seq, max_seq_len,
                                            partition_size, ctypes.byref(o))
@@ -186,7 +189,7 @@ class Decoder:
                  single_pass_max_len: Optional[int] = None, total_tokens_hint: int = 0,
                  num_cus: int = 0, per_query_head: bool = False,
                  fused_combine: bool = False, xcd_skew: int = 0, piece_cost: int = 0,
-                 stream_walk: int = 0, device="cuda"):
+                 stream_walk: int = 0, head_sequential: bool = False, device="cuda"):
         self.shape = (num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                       max_blocks_per_seq)
         self.dtype = dtype
@@ -194,11 +197,12 @@ class Decoder:
         self.partition_size = int(partition_size)
         self.opts = _opts(single_pass_max_len, num_cus, total_tokens_hint=total_tokens_hint,
                           per_query_head=per_query_head, fused_combine=fused_combine,
-                          xcd_skew=xcd_skew, piece_cost=piece_cost, stream_walk=stream_walk)
+                          xcd_skew=xcd_skew, piece_cost=piece_cost, stream_walk=stream_walk,
+                          head_sequential=head_sequential)
         nbytes = workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                                 max_blocks_per_seq, max_seq_len, partition_size,
                                 single_pass_max_len, total_tokens_hint, num_cus,
-                                per_query_head, stream_walk, fused_combine)
+                                per_query_head, stream_walk, fused_combine, head_sequential)
         self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
         self.workspace_bytes = nbytes
         if fused_combine and nbytes > 0:
@@ -245,7 +249,8 @@ def decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
            workspace: Optional[torch.Tensor] = None, single_pass_max_len: Optional[int] = None,
            events: Optional[Tuple[int, int]] = None, total_tokens_hint: int = 0,
            per_query_head: bool = False, fused_combine: bool = False,
-           xcd_skew: int = 0, piece_cost: int = 0, stream_walk: int = 0) -> torch.Tensor:
+           xcd_skew: int = 0, piece_cost: int = 0, stream_walk: int = 0,
+           head_sequential: bool = False) -> torch.Tensor:
     """One decode step: out[s,h] = softmax(scale q K^T) V over the paged caches.
 
     fused_combine: merge partitions inside phase 1; a workspace passed in must then
@@ -256,7 +261,7 @@ def decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
     mbps = block_tables.shape[1]
     need = workspace_size(S, Hq, Hkv, D, bs, mbps, max_seq_len, partition_size,
                           single_pass_max_len, total_tokens_hint, 0, per_query_head,
-                          stream_walk, fused_combine)
+                          stream_walk, fused_combine, head_sequential)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         if fused_combine:
@@ -265,7 +270,7 @@ def decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
         out = torch.empty_like(q)
     o = _opts(single_pass_max_len, events=events, total_tokens_hint=total_tokens_hint,
               per_query_head=per_query_head, fused_combine=fused_combine, xcd_skew=xcd_skew,
-              piece_cost=piece_cost, stream_walk=stream_walk)
+              piece_cost=piece_cost, stream_walk=stream_walk, head_sequential=head_sequential)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(lib().paged_attn_decode_ex(
         _ptr(out), _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),

@@ -566,7 +566,16 @@ __device__ __forceinline__ void finish_partial(const DecodeArgs& a, Phase1Lds<D,
 // fused combine the segment described by `mg` is merged by whichever workgroup
 // finishes its last partial.  Starts with a barrier, so LDS from a previous piece
 // may be reused.
-template <int D, class DT, int W>
+//
+// HS (the head-sequential ablation, page of commit 8d26e23, phase-1 kernel: the
+// group's query heads processed one after another): each staged tile is taken G
+// times, pass h computing QK^T, the softmax update and P.V for query head h alone
+// and re-reading K and V^T from LDS.  The MFMA tile still carries all 16 head
+// columns, so pass h zeroes the Q operand of the other columns, gives them P = 0 and
+// a rescale of 1, and leaves their state as it was: the accumulators are the same
+// registers as in the grouped pass, and every column's arithmetic is the grouped
+// one, so the result is bitwise the same, at G times the LDS reads and MFMAs.
+template <int D, class DT, int W, bool HS = false>
 __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& sm, int s,
                                           int unit, int t_begin, int t_end, bool final,
                                           long long rec, const SegMerge& mg) {
@@ -668,53 +677,102 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& 
         page_next = tile_pages(a.bt, s, t0 + 2 * kTile * W, t_end, bs, mbps);
     }
 
-    // S^T[token, head] = sum_d K[token, d] Q[head, d]
-    f32x4 st = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (!HS) {
+      // S^T[token, head] = sum_d K[token, d] Q[head, d]
+      f32x4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int off = Z::byte_off(col, 4 * ks + grp);
-      const u32x4 kop = *reinterpret_cast<const u32x4*>(ldsK + off);
-      const u32x4 qop = *reinterpret_cast<const u32x4*>(sm.q + off);
-      st = DT::mfma_qk(kop, qop, st);
-    }
+      for (int ks = 0; ks < KS; ++ks) {
+        const int off = Z::byte_off(col, 4 * ks + grp);
+        const u32x4 kop = *reinterpret_cast<const u32x4*>(ldsK + off);
+        const u32x4 qop = *reinterpret_cast<const u32x4*>(sm.q + off);
+        st = DT::mfma_qk(kop, qop, st);
+      }
 
-    // online softmax in base 2; this lane holds head `col`, tokens t0 + 4*grp + e
-    const int tk = t0 + 4 * grp;
-    float x[4];
+      // online softmax in base 2; this lane holds head `col`, tokens t0 + 4*grp + e
+      const int tk = t0 + 4 * grp;
+      float x[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = (tk + e < t_end) ? st[e] * a.scale_log2 : kNegInf;
-    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mx = xor_max<16>(mx);
-    mx = xor_max<32>(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    u32x2 p_hi, p_lo;
-    l_run = l_run * alpha + prob_operands<DT>(x, m_new, p_hi, p_lo);
+      for (int e = 0; e < 4; ++e) x[e] = (tk + e < t_end) ? st[e] * a.scale_log2 : kNegInf;
+      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      mx = xor_max<16>(mx);
+      mx = xor_max<32>(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      u32x2 p_hi, p_lo;
+      l_run = l_run * alpha + prob_operands<DT>(x, m_new, p_hi, p_lo);
 
-    // O^T[d, head] += sum_t V[t, d] P[head, t].  The A operand (lane: dim 16c + col,
-    // tokens 4*grp .. +3) is V^T; ds_read_b64_tr_b16 transposes it out of the
-    // row-major tile: within each 16-lane group, result lane i, element j comes
-    // from source lane i/4 + 4j, element i%4, so source lane r addresses row
-    // 4*grp + r/4, columns 16c + 4*(r%4) .. +3.
-    const bool tail = t0 + kTile > t_end;
-    uint32_t keep_lo = 0xffffffffu, keep_hi = 0xffffffffu;   // masks slots past the end
-    if (tail) {
-      const int n = t_end - tk;                                 // valid tokens of this lane
-      keep_lo = (n > 0 ? 0x0000ffffu : 0u) | (n > 1 ? 0xffff0000u : 0u);
-      keep_hi = (n > 2 ? 0x0000ffffu : 0u) | (n > 3 ? 0xffff0000u : 0u);
-    }
-    const int vrow = 4 * grp + (col >> 2);
+      // O^T[d, head] += sum_t V[t, d] P[head, t].  The A operand (lane: dim 16c + col,
+      // tokens 4*grp .. +3) is V^T; ds_read_b64_tr_b16 transposes it out of the
+      // row-major tile: within each 16-lane group, result lane i, element j comes
+      // from source lane i/4 + 4j, element i%4, so source lane r addresses row
+      // 4*grp + r/4, columns 16c + 4*(r%4) .. +3.
+      const bool tail = t0 + kTile > t_end;
+      uint32_t keep_lo = 0xffffffffu, keep_hi = 0xffffffffu;   // masks slots past the end
+      if (tail) {
+        const int n = t_end - tk;                                 // valid tokens of this lane
+        keep_lo = (n > 0 ? 0x0000ffffu : 0u) | (n > 1 ? 0xffff0000u : 0u);
+        keep_hi = (n > 2 ? 0x0000ffffu : 0u) | (n > 3 ? 0xffff0000u : 0u);
+      }
+      const int vrow = 4 * grp + (col >> 2);
 #pragma unroll
-    for (int c = 0; c < DB; ++c) {
-      const int vcol = 16 * c + 4 * (col & 3);
-      typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-      const i16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(ldsV + ZV::byte_off(vrow, vcol >> 3) + (vcol & 7) * 2));
-      u32x2 vop = __builtin_bit_cast(u32x2, raw);
-      vop.x &= keep_lo;
-      vop.y &= keep_hi;
-      acc[c] = pv_mfma<DT>(vop, p_hi, p_lo, acc[c] * alpha);
+      for (int c = 0; c < DB; ++c) {
+        const int vcol = 16 * c + 4 * (col & 3);
+        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+        const i16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(ldsV + ZV::byte_off(vrow, vcol >> 3) + (vcol & 7) * 2));
+        u32x2 vop = __builtin_bit_cast(u32x2, raw);
+        vop.x &= keep_lo;
+        vop.y &= keep_hi;
+        acc[c] = pv_mfma<DT>(vop, p_hi, p_lo, acc[c] * alpha);
+      }
+    } else {
+      // head-sequential: pass h updates query head h (column h) alone; the other
+      // columns get a zero Q operand, P = 0 and a rescale of 1
+      const int tk = t0 + 4 * grp;
+      const bool tail = t0 + kTile > t_end;
+      uint32_t keep_lo = 0xffffffffu, keep_hi = 0xffffffffu;
+      if (tail) {
+        const int n = t_end - tk;
+        keep_lo = (n > 0 ? 0x0000ffffu : 0u) | (n > 1 ? 0xffff0000u : 0u);
+        keep_hi = (n > 2 ? 0x0000ffffu : 0u) | (n > 3 ? 0xffff0000u : 0u);
+      }
+      const int vrow = 4 * grp + (col >> 2);
+      for (int h = 0; h < G; ++h) {
+        const bool live = col == h;
+        f32x4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int off = Z::byte_off(col, 4 * ks + grp);
+          const u32x4 kop = *reinterpret_cast<const u32x4*>(ldsK + off);
+          const u32x4 q = *reinterpret_cast<const u32x4*>(sm.q + off);
+          st = DT::mfma_qk(kop, live ? q : u32x4{0, 0, 0, 0}, st);
+        }
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (tk + e < t_end) ? st[e] * a.scale_log2 : kNegInf;
+        float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        mx = xor_max<16>(mx);
+        mx = xor_max<32>(mx);
+        const float m_new = live ? fmaxf(m_run, mx) : m_run;
+        const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+        m_run = m_new;
+        u32x2 p_hi, p_lo;
+        const float psum = prob_operands<DT>(x, m_new, p_hi, p_lo);
+        if (!live) p_hi = p_lo = u32x2{0u, 0u};
+        l_run = live ? l_run * alpha + psum : l_run;
+#pragma unroll
+        for (int c = 0; c < DB; ++c) {
+          const int vcol = 16 * c + 4 * (col & 3);
+          typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+          const i16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(ldsV + ZV::byte_off(vrow, vcol >> 3) + (vcol & 7) * 2));
+          u32x2 vop = __builtin_bit_cast(u32x2, raw);
+          vop.x &= keep_lo;
+          vop.y &= keep_hi;
+          acc[c] = pv_mfma<DT>(vop, p_hi, p_lo, acc[c] * alpha);
+        }
+      }
     }
   }
 
@@ -780,9 +838,10 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, Phase1Lds<D, W>& 
   if (!final && a.tickets != nullptr && mg.seg >= 0) finish_partial<D, DT, W>(a, sm, s, unit, mg);
 }
 
-// Grid mode: workgroup (partition, sequence, KV head), partition slowest.
-template <int D, class DT, int W>
-__global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_kernel(DecodeArgs a) {
+// Grid mode: workgroup (partition, sequence, KV head), partition slowest.  HS: the
+// head-sequential ablation (see run_piece).
+template <int D, class DT, int W, bool HS = false>
+__global__ __launch_bounds__(W * 64, HS ? 1 : 8 / W) void pa_phase1_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) Phase1Lds<D, W> sm;
   int wg = blockIdx.x;
   int unit, s, part;
@@ -833,7 +892,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pa_phase1_kernel(DecodeArgs a) 
     mg.rec0 = seg * a.max_parts;
     mg.step = 1;
   }
-  run_piece<D, DT, W>(a, sm, s, unit, t_begin, t_end, single, rec, mg);
+  run_piece<D, DT, W, HS>(a, sm, s, unit, t_begin, t_end, single, rec, mg);
 }
 
 // Balanced mode.  Sequence s has n(s) = ceil(L_s/16) tiles per KV head; laid end

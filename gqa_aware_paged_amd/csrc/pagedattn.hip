@@ -62,6 +62,7 @@ struct Plan {
   bool balanced = false; // length-balanced split (partition_size 0) vs fixed partitions
   bool stream = false;   // phase 1 as per-wave streams (pa_phase1_stream_kernel)
   bool parts = false;    // stream kernel with an explicit partition size
+  bool head_seq = false; // head-sequential ablation (fixed partitions)
   int P = 0;             // partition size (tokens), grid mode
   int T1 = 0;            // single-pass threshold (tokens), grid mode
   int max_parts = 0;     // partitions per (seq, kv head) slot; 0 = no phase 2, grid mode
@@ -138,6 +139,8 @@ int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int 
   // per-query-head ablation: one workgroup per query head (each KV page is then
   // read once per query head instead of once per KV head)
   const bool per_qhead = opt && opt->per_query_head;
+  // head-sequential ablation: the grouped fixed-partition grid, heads taken in turn
+  pl.head_seq = opt && opt->head_sequential;
   pl.units = per_qhead ? Hq : Hkv;
   pl.group = Hq / pl.units;
   pl.max_seq_len = max_len > 0 ? max_len : mbps * bs;
@@ -155,11 +158,11 @@ int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int 
   // the balanced kernel keeps its prefix of (virtual) tiles in 32-bit integers
   const long long max_tiles = (pl.max_seq_len + 15) / 16;
   const long long tiles_bound = static_cast<long long>(S) * (max_tiles + 1024);
-  pl.balanced = P_req == 0 && !forced_tier && !uniform && !per_qhead &&
+  pl.balanced = P_req == 0 && !forced_tier && !uniform && !per_qhead && !pl.head_seq &&
                 S <= pa::kMaxBalancedSeqs && tiles_bound <= std::numeric_limits<int>::max();
   // per-wave streams (the balanced split, and explicit partition sizes): not with the
   // fused combine or the per-query-head ablation, which keep one workgroup per piece
-  const bool stream_ok = !(opt && opt->stream_walk < 0) && !per_qhead &&
+  const bool stream_ok = !(opt && opt->stream_walk < 0) && !per_qhead && !pl.head_seq &&
                          !(opt && opt->fused_combine) && S <= pa::kMaxBalancedSeqs;
   const int pc_req = opt ? opt->piece_cost : 0;
   const int stream_pc = pc_req == 0 ? kStreamPieceCost : (pc_req < 0 ? 0 : (pc_req > 1024 ? 1024 : pc_req));
@@ -314,6 +317,9 @@ int launch_decode(const pa::DecodeArgs& args, const Plan& pl, hipStream_t stream
   else if (pl.balanced)
     hipLaunchKernelGGL((pa::pa_phase1_balanced_kernel<D, DT, kWaves>),
                        dim3(static_cast<unsigned>(pl.grid1)), dim3(kWaves * 64), 0, stream, args);
+  else if (pl.head_seq)
+    hipLaunchKernelGGL((pa::pa_phase1_kernel<D, DT, kWaves, true>),
+                       dim3(static_cast<unsigned>(pl.grid1)), dim3(kWaves * 64), 0, stream, args);
   else
     hipLaunchKernelGGL((pa::pa_phase1_kernel<D, DT, kWaves>),
                        dim3(static_cast<unsigned>(pl.grid1)), dim3(kWaves * 64), 0, stream, args);
@@ -442,6 +448,7 @@ PA_API int paged_attn_plan(const int32_t* seq_lens_host, int num_seqs, int num_h
   info->xcd_skew = pl.xcd_skew;
   info->piece_cost = pl.piece_cost;
   info->stream = pl.stream ? 1 : 0;
+  info->head_sequential = pl.head_seq ? 1 : 0;
   if (seq_lens_host) {
     if (pl.balanced) {
       // host mirror of the device split: sequence s covers virtual tiles

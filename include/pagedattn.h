@@ -155,6 +155,12 @@ typedef struct pa_options {
      * pages' dense (sequence, KV head, partition) grid for explicit partition
      * sizes). */
     int stream_walk;
+    /* Ablation only: 1 processes the group's query heads one after another inside
+     * each workgroup (page of commit 8d26e23, phase-1 kernel): every staged K/V tile
+     * is taken once per query head, re-read from LDS, with the MFMA operands of the
+     * other heads zeroed.  Bitwise equal to the grouped pass with the same partitions;
+     * uses fixed partitions (partition_size, or 0 as with equal lengths declared). */
+    int head_sequential;
 } pa_options;
 
 /* What a call will launch; filled by paged_attn_plan. */
@@ -176,6 +182,7 @@ typedef struct pa_plan_info {
     int xcd_skew;              /* XCD-paired shares in use (permille), 0 = equal */
     int piece_cost;            /* balanced split: tiles a piece start counts as */
     int stream;                /* 1: phase 1 walks per-wave streams (pa_options.stream_walk) */
+    int head_sequential;       /* 1: the head-sequential ablation (pa_options.head_sequential) */
 } pa_plan_info;
 
 /*

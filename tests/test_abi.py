@@ -126,6 +126,10 @@ def test_plan_matches_pages_grid(lib):
     assert st["phase1_workgroups"] == 256 and st["active_workgroups"] == 256
     assert st["workspace_bytes"] == info["workspace_bytes"]
     assert st["phase2_workgroups"] == info["phase2_workgroups"] == 4 * 16
+    # the head-sequential ablation keeps the grouped grid (heads taken in turn inside it)
+    hs = pa.plan(*args, single_pass_max_len=0, head_sequential=True)
+    assert hs["head_sequential"] == 1 and hs["stream"] == 0
+    assert hs["phase1_workgroups"] == g["blocks_per_kv_head_grid"]
     # the per-query-head ablation restores the pages' "before" grid
     info_q = pa.plan(*args, single_pass_max_len=0, per_query_head=True)
     assert info_q["phase1_workgroups"] == g["blocks_per_q_head_grid"] and info_q["stream"] == 0

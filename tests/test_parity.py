@@ -304,6 +304,34 @@ def test_per_query_head_ablation(P):
     assert_close(gpu_out(ablation), oracle_full(w), "per-query-head")
 
 
+@pytest.mark.parametrize("P", [256, 1024, 0])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_head_sequential_ablation(P, dtype):
+    """The group's query heads taken one after another per staged tile (the phase-1
+    kernel of the page of commit 8d26e23): each head's column is computed exactly as
+    in the grouped pass, so with the same partitions the outputs agree bit for bit
+    (P = 0: the automatic fixed partitions of equal lengths declared, on both)."""
+    say(f"case head-sequential ablation P={P} {dtype}")
+    lens = [1, 100, 700, 2000] if P else [3000] * 3
+    w = make(lens, partition_size=256, dtype=dtype, seed=60)
+    kw = dict(partition_size=P, max_seq_len=w.max_seq_len)
+    if P:
+        kw["single_pass_max_len"] = 0
+    else:
+        kw["total_tokens_hint"] = int(sum(lens))
+    info = pa.plan(lens, 24, 4, 256, 16, w.max_blocks_per_seq, w.max_seq_len, P,
+                   head_sequential=True, **{k: v for k, v in kw.items()
+                                             if k in ("single_pass_max_len", "total_tokens_hint")})
+    assert info["head_sequential"] == 1 and info["stream"] == 0 and info["balanced"] == 0
+    hs = pa.decode(w.q, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, w.scale,
+                   head_sequential=True, **kw)
+    grouped = pa.decode(w.q, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, w.scale,
+                        stream_walk=-1, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(hs, grouped)
+    assert_close(gpu_out(hs), oracle_full(w), f"head-sequential/P{P}/{dtype}")
+
+
 def test_workspace_reuse_and_stream():
     """A Decoder reuses one caller-owned workspace across calls and runs on a side stream."""
     say("case workspace reuse")
