@@ -29,7 +29,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0       # MI355X dense f16/bf16 MFMA
 COUNTERS = os.path.join(ROOT, "profiles", "pa_phase1_kernel_long-4x102400_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "gqa_aware_paged_amd", "csrc", f)
-                  for f in ("pa_kernels.h", "pagedattn.hip")]
+                  for f in ("pa_kernels.h", "pa_stream.h", "pagedattn.hip")]
 
 
 def log(msg):
@@ -170,6 +170,7 @@ def run_prefill(args, torch, pa, workloads):
         pa.prefill(w.q, w.k_new, w.v_new, c.key_cache, c.value_cache, c.block_tables,
                    c.seq_lens, w.query_start, c.scale, w.max_q_len, c.max_seq_len, out=out)
 
+    settle_steps = settle(torch, step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -187,7 +188,8 @@ def run_prefill(args, torch, pa, workloads):
     rec = {
         "metric": "prefill attention TFLOP/s (causal chunk over a paged context), 1 GPU",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1e3, 2),
+        "warmup": args.warmup, "settle": {"ms": args.settle_ms, "steps": settle_steps},
+        "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1e3, 2),
         "timing": "hot", "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": c.dtype, "data": "synthetic",
         "config": {"workload": w.name, "num_seqs": c.num_seqs,
@@ -226,11 +228,45 @@ def run_prefill(args, torch, pa, workloads):
     print(json.dumps(rec), flush=True)
 
 
+def settle(torch, step, ms: float) -> int:
+    """Untimed steps of the workload itself until `ms` of wall time have passed.  For
+    the first ~10-25 ms of a memory-bound workload on a freshly loaded MI355X the step
+    times wander by up to 25 % before they settle (a fill kernel of the same duration
+    does not remove it; the workload's own steps do), so the timed steps follow this."""
+    n = 0
+    t0 = time.perf_counter()
+    while ms > 0 and time.perf_counter() - t0 < ms * 1e-3:
+        step()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
+def copy_probe(args, torch, dev):
+    """One device-to-device copy of a known size, for scaling the byte counters of a
+    profiled run (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)."""
+    if args.copy_probe_mib <= 0:
+        return
+    n = args.copy_probe_mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy probe: {n} bytes read, {n} bytes written")
+    del src, dst
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=50.0,
+                    help="untimed steps of the workload for this long before the warmup "
+                         "steps (0 = none)")
     ap.add_argument("--workload", default="long",
                     choices=["tiny", "batch", "long", "mixed", "saturation", "prefill"])
     ap.add_argument("--partition-size", type=int, default=0,
@@ -293,6 +329,7 @@ def main():
     pa.lib()
 
     if args.workload == "prefill":
+        copy_probe(args, torch, dev)
         run_prefill(args, torch, pa, workloads)
         return
     log(f"generating workload {args.workload}")
@@ -326,15 +363,7 @@ def main():
                    head_sequential=args.head_sequential)
     log(f"plan: {info}")
 
-    if args.copy_probe_mib > 0:
-        n = args.copy_probe_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"copy probe: {n} bytes read, {n} bytes written")
-        del src, dst
+    copy_probe(args, torch, dev)
 
     ev = HipEvents()
     stream = torch.cuda.current_stream(dev)
@@ -362,10 +391,11 @@ def main():
                 ev.destroy(b)
         return ms, ph1
 
+    settle_steps = settle(torch, lambda: step(dec), args.settle_ms)
     for _ in range(args.warmup):
         step(dec)
     torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps)")
+    log(f"settle {settle_steps} steps ({args.settle_ms} ms), warmup done ({args.warmup} steps)")
 
     # timed region 1: K plain steps -> ms_per_step
     t0 = time.perf_counter()
@@ -432,6 +462,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"ms": args.settle_ms, "steps": settle_steps},
         "ms_per_step": round(head_ms, 5),
         "us_per_step": round(head_ms * 1e3, 2),
         "timing": timing,

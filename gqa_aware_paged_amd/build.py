@@ -9,6 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "pagedattn.hip")
 DEPS = [SRC, os.path.join(PKG, "csrc", "pa_kernels.h"), os.path.join(PKG, "csrc", "pa_prefill.h"),
+        os.path.join(PKG, "csrc", "pa_stream.h"),
         os.path.join(ROOT, "include", "pagedattn.h")]
 SO = os.path.join(PKG, "libpagedattn.so")
 
