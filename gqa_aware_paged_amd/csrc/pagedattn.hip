@@ -649,12 +649,11 @@ namespace {
 
 template <int D, class DT>
 void launch_prefill(const pa::PrefillArgs& args, unsigned grid, hipStream_t stream) {
+  const dim3 block(pa::kPrefillWaves * 64);
   if (args.block_size == 8)
-    hipLaunchKernelGGL((pa::pa_prefill_kernel<D, DT, 1>), dim3(grid),
-                       dim3(pa::kPrefillWaves * 64), 0, stream, args);
+    hipLaunchKernelGGL((pa::pa_prefill_kernel<D, DT, 1>), dim3(grid), block, 0, stream, args);
   else
-    hipLaunchKernelGGL((pa::pa_prefill_kernel<D, DT, 2>), dim3(grid),
-                       dim3(pa::kPrefillWaves * 64), 0, stream, args);
+    hipLaunchKernelGGL((pa::pa_prefill_kernel<D, DT, 2>), dim3(grid), block, 0, stream, args);
 }
 
 // Division by the page size as a multiply-high and a shift (Granlund-Montgomery
