@@ -33,6 +33,7 @@
 namespace pa {
 
 constexpr int kStreamMaxGroup = 16;       // query heads per KV head (the largest group served)
+constexpr float kLazyRescaleLog2 = 8.f;   // slack of the running max before a rescale (base 2)
 
 template <int D, int W>
 struct StreamLds {
@@ -380,11 +381,21 @@ __global__ __launch_bounds__(W * 64, 1) void pa_phase1_stream_kernel(DecodeArgs 
       float mx = fmaxf(fmaxf(xv[0], xv[1]), fmaxf(xv[2], xv[3]));
       mx = xor_max<16>(mx);
       mx = xor_max<32>(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+      // Lazy rescale: the running max moves only when a head's tile max exceeds it by
+      // more than 2^kLazyRescaleLog2 (a wave-uniform branch); otherwise the tile's
+      // probabilities are taken against the old max (each at most 2^8, inside f16
+      // and bf16) and the accumulators keep their scale.  The first tile of a piece
+      // always moves it (the running max is -inf and every head has a key there).
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescaleLog2) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int cc = 0; cc < DB; ++cc) acc[cc] *= alpha;
+      }
       u32x2 p_hi, p_lo;
-      l_run = l_run * alpha + prob_operands<DT>(xv, m_new, p_hi, p_lo);
+      l_run += prob_operands<DT>(xv, m_run, p_hi, p_lo);
       // O^T[d, head] += sum_t V[t, d] P[head, t]: V^T read transposed out of the tile
       const bool tail = t0 + kTile > cL;
       uint32_t keep_lo = 0xffffffffu, keep_hi = 0xffffffffu;   // masks slots past the end
@@ -403,7 +414,7 @@ __global__ __launch_bounds__(W * 64, 1) void pa_phase1_stream_kernel(DecodeArgs 
         u32x2 vop = __builtin_bit_cast(u32x2, raw);
         vop.x &= keep_lo;
         vop.y &= keep_hi;
-        acc[cc] = pv_mfma<DT>(vop, p_hi, p_lo, acc[cc] * alpha);
+        acc[cc] = pv_mfma<DT>(vop, p_hi, p_lo, acc[cc]);
       }
 
       // the piece ends with this tile and the wave goes on: finish it from registers
