@@ -43,7 +43,8 @@ class PlanInfo(ctypes.Structure):
                 ("threads_per_workgroup", ctypes.c_int), ("lds_bytes_phase1", ctypes.c_int),
                 ("balanced", ctypes.c_int), ("fused", ctypes.c_int),
                 ("xcd_skew", ctypes.c_int), ("piece_cost", ctypes.c_int),
-                ("stream", ctypes.c_int), ("head_sequential", ctypes.c_int)]
+                ("stream", ctypes.c_int), ("head_sequential", ctypes.c_int),
+                ("reduce_slices", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -75,7 +75,7 @@ struct Plan {
   long long records = 0; // partial records in the workspace
   long long grid1 = 0, grid2 = 0;
   bool fused = false;    // partials merged in phase 1 (ticket counters), no phase 2
-  bool wide_reduce = false;  // phase 2 takes balanced_slices(D) slices per workgroup
+  int reduce_slices = 1;     // 16-wide head_dim slices per phase-2 workgroup
   size_t ws_acc_off = 0, ws_ml_off = 0, ws_jobs_off = 0, ws_bytes = 0;
 };
 
@@ -206,7 +206,7 @@ int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int 
     pl.records = 2LL * pl.num_wg;
     pl.grid1 = pl.num_wg;
     pl.grid2 = static_cast<long long>(pl.num_wg) * (D / 16 / balanced_slices(D));
-    pl.wide_reduce = true;
+    pl.reduce_slices = balanced_slices(D);
     pl.T1 = -1;
   } else if (stream_parts) {
     // the pages' partitions of P tokens, one partial each, walked by per-wave streams
@@ -239,12 +239,26 @@ int make_plan(int S, int Hq, int Hkv, int D, int bs, int mbps, int max_len, int 
     pl.records = static_cast<long long>(S) * pl.units * pl.max_parts;
   }
   if (!pl.balanced && pl.max_parts > 0) {
-    // phase 2 of fixed partitions: wide workgroups (fewer of them) when one round of
-    // loads covers a segment's partials, else one 16-wide slice per workgroup
-    const int per_round = pa::kRedThreads / (4 * balanced_slices(D)) * pa::reduce_unroll(pl.group);
-    pl.wide_reduce = pl.max_parts <= per_round;
-    pl.grid2 = static_cast<long long>(S) * pl.units *
-               (D / 16 / (pl.wide_reduce ? balanced_slices(D) : 1));
+    // Phase 2 of fixed partitions: a workgroup takes `slices` 16-wide head_dim slices
+    // of one segment and folds its partials kRedThreads / (4 * slices) * unroll at a
+    // time.  Wider workgroups are fewer but need more rounds for a long segment.
+    // Measured on MI355X (D 256, 6 heads per group, 16 to 256 segments of up to 400
+    // partials): about 1 us per round of the longest segment and 6 ns per workgroup,
+    // so the width with the least rounds * 1000 + workgroups * 6 (ns) is taken.
+    const long long segs = static_cast<long long>(S) * pl.units;
+    long long best_cost = std::numeric_limits<long long>::max();
+    for (const int spw : {1, 2, 4, balanced_slices(D)}) {
+      if (spw > balanced_slices(D)) continue;
+      const int per_round = pa::kRedThreads / (4 * spw) * pa::reduce_unroll(pl.group);
+      const long long rounds = (pl.max_parts + per_round - 1) / per_round;
+      const long long wgs = segs * (D / 16 / spw);
+      const long long cost = rounds * 1000 + wgs * 6;
+      if (cost <= best_cost) {             // ties go to the wider workgroup
+        best_cost = cost;
+        pl.reduce_slices = spw;
+      }
+    }
+    pl.grid2 = segs * (D / 16 / pl.reduce_slices);
   }
   if (pl.grid1 > std::numeric_limits<int>::max() || pl.grid2 > std::numeric_limits<int>::max())
     return PA_ERR_SHAPE;
@@ -268,35 +282,40 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 // Phase 2 is instantiated per group size so its loads can all be in flight at once.
 template <int D, class DT, int G>
-void launch_reduce_g(bool wide, unsigned grid, hipStream_t stream, const pa::DecodeArgs& args) {
-  if (wide)
-    hipLaunchKernelGGL((pa::pa_reduce_kernel<D, DT, G, balanced_slices(D)>), dim3(grid),
-                       dim3(pa::kRedThreads), 0, stream, args);
-  else
-    hipLaunchKernelGGL((pa::pa_reduce_kernel<D, DT, G, 1>), dim3(grid), dim3(pa::kRedThreads), 0,
-                       stream, args);
+void launch_reduce_g(int slices, unsigned grid, hipStream_t stream, const pa::DecodeArgs& args) {
+  const dim3 block(pa::kRedThreads);
+  switch (slices) {
+    case 1: hipLaunchKernelGGL((pa::pa_reduce_kernel<D, DT, G, 1>), dim3(grid), block, 0, stream, args); break;
+    case 2: hipLaunchKernelGGL((pa::pa_reduce_kernel<D, DT, G, 2>), dim3(grid), block, 0, stream, args); break;
+    case 4: hipLaunchKernelGGL((pa::pa_reduce_kernel<D, DT, G, 4>), dim3(grid), block, 0, stream, args); break;
+    default:
+      if constexpr (balanced_slices(D) > 4)
+        hipLaunchKernelGGL((pa::pa_reduce_kernel<D, DT, G, balanced_slices(D)>), dim3(grid), block,
+                           0, stream, args);
+      break;
+  }
 }
 
 template <int D, class DT>
-int launch_reduce(int group, bool wide, unsigned grid, hipStream_t stream,
+int launch_reduce(int group, int slices, unsigned grid, hipStream_t stream,
                   const pa::DecodeArgs& args) {
   switch (group) {
-    case 1: launch_reduce_g<D, DT, 1>(wide, grid, stream, args); break;
-    case 2: launch_reduce_g<D, DT, 2>(wide, grid, stream, args); break;
-    case 3: launch_reduce_g<D, DT, 3>(wide, grid, stream, args); break;
-    case 4: launch_reduce_g<D, DT, 4>(wide, grid, stream, args); break;
-    case 5: launch_reduce_g<D, DT, 5>(wide, grid, stream, args); break;
-    case 6: launch_reduce_g<D, DT, 6>(wide, grid, stream, args); break;
-    case 7: launch_reduce_g<D, DT, 7>(wide, grid, stream, args); break;
-    case 8: launch_reduce_g<D, DT, 8>(wide, grid, stream, args); break;
-    case 9: launch_reduce_g<D, DT, 9>(wide, grid, stream, args); break;
-    case 10: launch_reduce_g<D, DT, 10>(wide, grid, stream, args); break;
-    case 11: launch_reduce_g<D, DT, 11>(wide, grid, stream, args); break;
-    case 12: launch_reduce_g<D, DT, 12>(wide, grid, stream, args); break;
-    case 13: launch_reduce_g<D, DT, 13>(wide, grid, stream, args); break;
-    case 14: launch_reduce_g<D, DT, 14>(wide, grid, stream, args); break;
-    case 15: launch_reduce_g<D, DT, 15>(wide, grid, stream, args); break;
-    case 16: launch_reduce_g<D, DT, 16>(wide, grid, stream, args); break;
+    case 1: launch_reduce_g<D, DT, 1>(slices, grid, stream, args); break;
+    case 2: launch_reduce_g<D, DT, 2>(slices, grid, stream, args); break;
+    case 3: launch_reduce_g<D, DT, 3>(slices, grid, stream, args); break;
+    case 4: launch_reduce_g<D, DT, 4>(slices, grid, stream, args); break;
+    case 5: launch_reduce_g<D, DT, 5>(slices, grid, stream, args); break;
+    case 6: launch_reduce_g<D, DT, 6>(slices, grid, stream, args); break;
+    case 7: launch_reduce_g<D, DT, 7>(slices, grid, stream, args); break;
+    case 8: launch_reduce_g<D, DT, 8>(slices, grid, stream, args); break;
+    case 9: launch_reduce_g<D, DT, 9>(slices, grid, stream, args); break;
+    case 10: launch_reduce_g<D, DT, 10>(slices, grid, stream, args); break;
+    case 11: launch_reduce_g<D, DT, 11>(slices, grid, stream, args); break;
+    case 12: launch_reduce_g<D, DT, 12>(slices, grid, stream, args); break;
+    case 13: launch_reduce_g<D, DT, 13>(slices, grid, stream, args); break;
+    case 14: launch_reduce_g<D, DT, 14>(slices, grid, stream, args); break;
+    case 15: launch_reduce_g<D, DT, 15>(slices, grid, stream, args); break;
+    case 16: launch_reduce_g<D, DT, 16>(slices, grid, stream, args); break;
     default: return PA_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -328,7 +347,7 @@ int launch_decode(const pa::DecodeArgs& args, const Plan& pl, hipStream_t stream
     if (hipEventRecord(opt->phase1_end, stream) != hipSuccess) return PA_ERR_HIP;
   }
   if (pl.grid2 > 0) {
-    const int st = launch_reduce<D, DT>(pl.group, pl.wide_reduce, static_cast<unsigned>(pl.grid2),
+    const int st = launch_reduce<D, DT>(pl.group, pl.reduce_slices, static_cast<unsigned>(pl.grid2),
                                         stream, args);
     if (st != PA_OK) return st;
   }
@@ -440,6 +459,7 @@ PA_API int paged_attn_plan(const int32_t* seq_lens_host, int num_seqs, int num_h
   info->group = pl.group;
   info->phase1_workgroups = pl.grid1;
   info->phase2_workgroups = pl.grid2;
+  info->reduce_slices = pl.grid2 > 0 ? pl.reduce_slices : 0;
   info->workspace_bytes = pl.ws_bytes;
   info->threads_per_workgroup = kWaves * 64;
   info->lds_bytes_phase1 = kWaves * 2 * pa::kTile * head_dim * 2;

@@ -183,6 +183,7 @@ typedef struct pa_plan_info {
     int piece_cost;            /* balanced split: tiles a piece start counts as */
     int stream;                /* 1: phase 1 walks per-wave streams (pa_options.stream_walk) */
     int head_sequential;       /* 1: the head-sequential ablation (pa_options.head_sequential) */
+    int reduce_slices;         /* 16-wide head_dim slices per phase-2 workgroup (0 = no phase 2) */
 } pa_plan_info;
 
 /*

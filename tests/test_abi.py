@@ -426,3 +426,27 @@ def test_balanced_cut_matches_formula(lib, seed):
         single, split = _split_counts(lens, ns, sk, pc)
         assert (info["single_pass_seqs"], info["partitioned_seqs"]) == (single, split), \
             (skew, cost, ns)
+
+
+def test_phase2_width_follows_rounds_and_grid(lib):
+    """Fixed partitions: the phase-2 workgroup width (16-wide slices) is the one with
+    the least (rounds of the longest segment) x 1 us + workgroups x 6 ns: one slice
+    for a few long segments, wider for many segments.  These are the widths measured
+    fastest on MI355X for each case."""
+    import workloads
+    mixed, batch = list(workloads.mixed_lens()), list(workloads.batch_lens())
+
+    def width(lens, P):
+        mb = (max(lens) + 15) // 16
+        info = pa.plan(lens, 24, 4, 256, 16, mb, max(lens), P)
+        assert info["phase2_workgroups"] == len(lens) * 4 * (16 // info["reduce_slices"])
+        return info["reduce_slices"]
+
+    assert width([102400] * 4, 256) == 1 and width([102400] * 4, 512) == 1
+    assert width(mixed, 256) == 4 and width(mixed, 512) == 4 and width(mixed, 1024) == 8
+    assert width(batch, 256) == 8 and width(batch, 512) == 8
+    # the balanced split's phase 2 always takes the widest workgroups; no phase 2 -> 0
+    assert pa.plan(mixed, 24, 4, 256, 16, 4096, 65536, 0)["reduce_slices"] == 8
+    assert pa.plan([10] * 3, 24, 4, 256, 16, 1, 10, 0, total_tokens_hint=30)["reduce_slices"] == 0
+    # head_dim 64 has 4 slices in all
+    assert pa.plan(mixed, 24, 4, 64, 16, 4096, 65536, 1024)["reduce_slices"] <= 4
