@@ -36,7 +36,7 @@ constexpr int kStreamMaxGroup = 16;       // query heads per KV head (the larges
 constexpr float kLazyRescaleLog2 = 8.f;   // slack of the running max before a rescale (base 2)
 
 template <int D, int W>
-struct StreamLds {
+struct StreamLdsCore {
   static constexpr int kTileBytes = kTile * D * 2;
   // a state of G <= kStreamMaxGroup heads, packed: f32x4 (cc*G + h)*4 + q4 holds head
   // h, dims 16*cc + 4*q4 .. +3
@@ -49,6 +49,28 @@ struct StreamLds {
   int preR[kMaxBalancedSeqs + 1];            // real tiles of the sequences before s
   int len[kMaxBalancedSeqs];                 // lengths clamped to [0, max_seq_len]
   int wave_tot[2][W];
+};
+
+// LDS a stream workgroup may take: one workgroup per CU at head_dim 256, two below
+// (160 KiB per CU).
+template <int D>
+constexpr int stream_lds_budget() { return (D >= 256 ? 160 : 80) * 1024; }
+
+// The rest of that budget is a pool of partial records (PARTS).  A record stored
+// while the wave's K/V reads stream costs about ten times its bytes (stores mixed
+// into the saturated read stream); the same store after the walk costs about its
+// bytes.  So a record that a wave finishes before the end of its run takes a free
+// slot of the pool if there is one and is written out by the whole workgroup after
+// the walk.  Slot: the packed output (f32x4 (cc*G + h)*4 + q4), then (max, exp sum)
+// of each head (8 f32x4 hold 16 heads), then the record index.
+template <int D, int W>
+struct StreamLds : StreamLdsCore<D, W> {
+  static constexpr int kPoolF4 =
+      (stream_lds_budget<D>() - static_cast<int>(sizeof(StreamLdsCore<D, W>)) - 64) / 16;
+  static_assert(kPoolF4 >= 0, "the core layout must fit the LDS budget");
+  int pool_next;                             // slots taken (may pass the slot count)
+  int pool_pad[3];
+  f32x4 pool[kPoolF4 > 0 ? kPoolF4 : 1];
 };
 
 template <int D, class DT, int W, bool PARTS>
@@ -115,6 +137,7 @@ __global__ __launch_bounds__(W * 64, 1) void pa_phase1_stream_kernel(DecodeArgs 
       sm.wave_tot[1][wave] = ir;
     }
     if (tid < W - 1) sm.park_start[tid] = -1;
+    if (tid == 0) sm.pool_next = 0;
     __syncthreads();
     int bc = ic - csum, br = ir - rsum;
     for (int v = 0; v < wave; ++v) {
@@ -243,6 +266,28 @@ __global__ __launch_bounds__(W * 64, 1) void pa_phase1_stream_kernel(DecodeArgs 
         if (grp == 0) a.ws_ml[dest * G + col] = make_float2(M, Lsum);
       }
     }
+  };
+  // a record finished inside the walk: into a pool slot if one is free (the whole
+  // workgroup writes the pool out after the walk); false if the pool is full
+  const int kp4 = DB * G * 4;                        // packed f32x4 of one record
+  const int slot_f4 = kp4 + 9;
+  const int n_slots = PARTS ? StreamLds<D, W>::kPoolF4 / slot_f4 : 0;
+  auto pool_piece = [&](long long dest, float M, float Lsum) -> bool {
+    if (n_slots == 0) return false;
+    int slot = 0;
+    if (lane == 0)
+      slot = __hip_atomic_fetch_add(&sm.pool_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    slot = __builtin_amdgcn_readfirstlane(slot);
+    if (slot >= n_slots) return false;
+    f32x4* base = sm.pool + slot * slot_f4;
+    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+    if (col < G) {
+#pragma unroll
+      for (int cc = 0; cc < DB; ++cc) base[(cc * G + col) * 4 + grp] = acc[cc] * inv;
+      if (grp == 0) reinterpret_cast<float2*>(base + kp4)[col] = make_float2(M, Lsum);
+    }
+    if (lane == 0) *reinterpret_cast<long long*>(base + kp4 + 8) = dest;
+    return true;
   };
   // a later wave's first piece, begun by an earlier wave: parked for the merge
   auto park = [&](int ps, float M, float Lsum) {
@@ -421,8 +466,12 @@ __global__ __launch_bounds__(W * 64, 1) void pa_phase1_stream_kernel(DecodeArgs 
       // (or park it, if an earlier wave began it) and start the next one
       if (more && x + 1 == pe) {
         const float Ls = full_sum();
-        if (ps >= wa) write_piece(dest_of(p_s, ps, pe), m_run, Ls);
-        else park(ps, m_run, Ls);
+        if (ps >= wa) {
+          const long long dest = dest_of(p_s, ps, pe);
+          if (dest < 0 || !pool_piece(dest, m_run, Ls)) write_piece(dest, m_run, Ls);
+        } else {
+          park(ps, m_run, Ls);
+        }
         m_run = kNegInf;
         l_run = 0.f;
 #pragma unroll
@@ -444,6 +493,20 @@ __global__ __launch_bounds__(W * 64, 1) void pa_phase1_stream_kernel(DecodeArgs 
   }
   // pieces cut by range boundaries: the first wave holding one merges the parked parts
   __syncthreads();
+  if constexpr (PARTS) {
+    // the pooled records, written by the whole workgroup
+    const int used = min(uniform(sm.pool_next), n_slots);
+    for (int sl = 0; sl < used; ++sl) {
+      const f32x4* base = sm.pool + sl * slot_f4;
+      const long long d = *reinterpret_cast<const long long*>(base + kp4 + 8);
+      for (int i = tid; i < kp4; i += NT) {
+        const int cc = i / (4 * G), rem = i - cc * 4 * G;
+        *reinterpret_cast<f32x4*>(a.ws_acc + rec_acc_index(cc, d, rem >> 2, G, a.records) +
+                                  4 * (rem & 3)) = base[i];
+      }
+      if (tid < G) a.ws_ml[d * G + tid] = reinterpret_cast<const float2*>(base + kp4)[tid];
+    }
+  }
   if (merger) {
     float M = m_run, Lsum = kept_l;
     for (int v = wave + 1; v < W; ++v) {
