@@ -18,14 +18,16 @@
 // product of the current one has been issued, the online-softmax state (max, exp
 // sum, accumulator) in registers.  No barrier and no merge stand between the
 // pieces of a range: a piece that lies inside one range is finished from
-// registers (its output rows, or its partial record) while the next tile's loads
-// are in flight.  Only a piece cut by a range boundary is shared: each later wave
-// holding part of it parks its state in LDS (at most one per wave, its first
-// piece), and after the walk the first wave holding it merges the parked parts with
-// the flash-attention rescale and writes the result.  Records, phase 2 and the job
-// list are those of the other kernels: PARTS uses the fixed-partition record of
-// (sequence, KV head, partition) and the fixed-partition phase 2; the balanced
-// split the two records per workgroup.
+// registers (its output rows), or, for a partial record, parked in a free slot of
+// an LDS pool that the whole workgroup writes out after the walk (stored directly
+// when the pool is full: stores mixed into the saturated read stream cost about
+// ten times their bytes).  Only a piece cut by a range boundary is shared: each
+// later wave holding part of it parks its state in a reserved pool slot (at most
+// one per wave, its first piece), and after the walk the first wave holding it
+// merges the parked parts with the flash-attention rescale and writes the result.
+// Records, phase 2 and the job list are those of the other kernels: PARTS uses the
+// fixed-partition record of (sequence, KV head, partition) and the fixed-partition
+// phase 2; the balanced split the two records per workgroup.
 #pragma once
 
 #include "pa_kernels.h"
@@ -42,9 +44,7 @@ struct StreamLdsCore {
   // h, dims 16*cc + 4*q4 .. +3
   static constexpr int kPack = (D / 16) * kStreamMaxGroup * 4;
   unsigned char tiles[W * 2 * kTileBytes];   // per wave: K tile, V tile
-  f32x4 park_acc[W - 1][kPack];              // first piece of waves 1..W-1, if shared
-  float2 park_ml[W - 1][kStreamMaxGroup];    // its (max, exp sum) per head
-  int park_start[W - 1];                     // its first real tile in the share, or -1
+  int park_start[W - 1];                     // first real tile of wave v+1's parked piece, or -1
   int pre[kMaxBalancedSeqs + 1];             // virtual tiles of the sequences before s
   int preR[kMaxBalancedSeqs + 1];            // real tiles of the sequences before s
   int len[kMaxBalancedSeqs];                 // lengths clamped to [0, max_seq_len]
@@ -56,18 +56,21 @@ struct StreamLdsCore {
 template <int D>
 constexpr int stream_lds_budget() { return (D >= 256 ? 160 : 80) * 1024; }
 
-// The rest of that budget is a pool of partial records (PARTS).  A record stored
-// while the wave's K/V reads stream costs about ten times its bytes (stores mixed
-// into the saturated read stream); the same store after the walk costs about its
-// bytes.  So a record that a wave finishes before the end of its run takes a free
-// slot of the pool if there is one and is written out by the whole workgroup after
-// the walk.  Slot: the packed output (f32x4 (cc*G + h)*4 + q4), then (max, exp sum)
-// of each head (8 f32x4 hold 16 heads), then the record index.
+// The rest of that budget is a pool of slots, each a piece's state packed: the
+// accumulator (f32x4 (cc*G + h)*4 + q4), then (max, exp sum) of each head (8 f32x4
+// hold 16 heads), then a record index.  Slots 0..W-2 hold the first piece of waves
+// 1..W-1 when an earlier wave began it (parked for the merge after the walk).  The
+// others hold partial records (PARTS): a record stored while the wave's K/V reads
+// stream costs about ten times its bytes (stores mixed into the saturated read
+// stream), the same store after the walk about its bytes, so a record that a wave
+// finishes before the end of its run takes a free slot if there is one and the
+// whole workgroup writes the pool out after the walk.
 template <int D, int W>
 struct StreamLds : StreamLdsCore<D, W> {
   static constexpr int kPoolF4 =
       (stream_lds_budget<D>() - static_cast<int>(sizeof(StreamLdsCore<D, W>)) - 64) / 16;
-  static_assert(kPoolF4 >= 0, "the core layout must fit the LDS budget");
+  static_assert(kPoolF4 >= (W - 1) * (StreamLdsCore<D, W>::kPack + 9),
+                "the parked pieces of the largest group must fit the pool");
   int pool_next;                             // slots taken (may pass the slot count)
   int pool_pad[3];
   f32x4 pool[kPoolF4 > 0 ? kPoolF4 : 1];
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(W * 64, 1) void pa_phase1_stream_kernel(DecodeArgs 
       sm.wave_tot[1][wave] = ir;
     }
     if (tid < W - 1) sm.park_start[tid] = -1;
-    if (tid == 0) sm.pool_next = 0;
+    if (tid == 0) sm.pool_next = W - 1;      // slots 0..W-2: parked pieces
     __syncthreads();
     int bc = ic - csum, br = ir - rsum;
     for (int v = 0; v < wave; ++v) {
@@ -273,7 +276,7 @@ __global__ __launch_bounds__(W * 64, 1) void pa_phase1_stream_kernel(DecodeArgs 
   const int slot_f4 = kp4 + 9;
   const int n_slots = PARTS ? StreamLds<D, W>::kPoolF4 / slot_f4 : 0;
   auto pool_piece = [&](long long dest, float M, float Lsum) -> bool {
-    if (n_slots == 0) return false;
+    if (n_slots <= W - 1) return false;
     int slot = 0;
     if (lane == 0)
       slot = __hip_atomic_fetch_add(&sm.pool_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -293,10 +296,11 @@ __global__ __launch_bounds__(W * 64, 1) void pa_phase1_stream_kernel(DecodeArgs 
   auto park = [&](int ps, float M, float Lsum) {
     if (wave == 0) return;       // never: wave 0's pieces all begin inside its run
     const int v = wave - 1;
+    f32x4* base = sm.pool + v * slot_f4;
     if (col < G) {
 #pragma unroll
-      for (int cc = 0; cc < DB; ++cc) sm.park_acc[v][(cc * G + col) * 4 + grp] = acc[cc];
-      if (grp == 0) sm.park_ml[v][col] = make_float2(M, Lsum);
+      for (int cc = 0; cc < DB; ++cc) base[(cc * G + col) * 4 + grp] = acc[cc];
+      if (grp == 0) reinterpret_cast<float2*>(base + kp4)[col] = make_float2(M, Lsum);
     }
     if (lane == 0) sm.park_start[v] = ps;
   };
@@ -496,7 +500,7 @@ __global__ __launch_bounds__(W * 64, 1) void pa_phase1_stream_kernel(DecodeArgs 
   if constexpr (PARTS) {
     // the pooled records, written by the whole workgroup
     const int used = min(uniform(sm.pool_next), n_slots);
-    for (int sl = 0; sl < used; ++sl) {
+    for (int sl = W - 1; sl < used; ++sl) {
       const f32x4* base = sm.pool + sl * slot_f4;
       const long long d = *reinterpret_cast<const long long*>(base + kp4 + 8);
       for (int i = tid; i < kp4; i += NT) {
@@ -511,15 +515,16 @@ __global__ __launch_bounds__(W * 64, 1) void pa_phase1_stream_kernel(DecodeArgs 
     float M = m_run, Lsum = kept_l;
     for (int v = wave + 1; v < W; ++v) {
       if (uniform(sm.park_start[v - 1]) != ps) continue;   // no part of this piece
-      const float2 ml = col < G ? sm.park_ml[v - 1][col] : make_float2(kNegInf, 0.f);
+      const f32x4* base = sm.pool + (v - 1) * slot_f4;
+      const float2 ml =
+          col < G ? reinterpret_cast<const float2*>(base + kp4)[col] : make_float2(kNegInf, 0.f);
       const float Mn = fmaxf(M, ml.x);
       const float f = Mn == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
       const float fv = Mn == kNegInf ? 0.f : __builtin_amdgcn_exp2f(ml.x - Mn);
       Lsum = Lsum * f + ml.y * fv;
 #pragma unroll
       for (int cc = 0; cc < DB; ++cc) {
-        const f32x4 pv = col < G ? sm.park_acc[v - 1][(cc * G + col) * 4 + grp]
-                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 pv = col < G ? base[(cc * G + col) * 4 + grp] : f32x4{0.f, 0.f, 0.f, 0.f};
         acc[cc] = acc[cc] * f + pv * fv;
       }
       M = Mn;
