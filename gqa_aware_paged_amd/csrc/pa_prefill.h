@@ -104,6 +104,40 @@ __device__ __forceinline__ float add_pair(uint32_t w, float acc) {
                                   f16x2{(_Float16)1.f, (_Float16)1.f}, acc, false);
 }
 
+// Two probabilities rounded (to nearest even) to the element type and packed, in one
+// conversion instruction (v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32 on gfx950).
+template <class DT>
+__device__ __forceinline__ uint32_t pack_pair(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  if constexpr (DT::kSplitP) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+  } else {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+  }
+}
+
+// P.V MFMA operands p_e = 2^arg_e rounded to the element type (hi + lo with
+// kSplitP), with packed conversions; the exp sum is taken separately.
+template <class DT>
+__device__ __forceinline__ void prefill_probs(const float (&arg)[4], u32x2& hi, u32x2& lo) {
+  float p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(arg[e]);
+  hi = u32x2{pack_pair<DT>(p[0], p[1]), pack_pair<DT>(p[2], p[3])};
+  if constexpr (DT::kSplitP) {
+    // the remainders p - hi are exact in fp32; a bf16 value is its bits << 16
+    const float h0 = __builtin_bit_cast(float, hi.x << 16);
+    const float h1 = __builtin_bit_cast(float, hi.x & 0xffff0000u);
+    const float h2 = __builtin_bit_cast(float, hi.y << 16);
+    const float h3 = __builtin_bit_cast(float, hi.y & 0xffff0000u);
+    lo = u32x2{pack_pair<DT>(p[0] - h0, p[1] - h1), pack_pair<DT>(p[2] - h2, p[3] - h3)};
+  } else {
+    lo = u32x2{0u, 0u};
+  }
+}
+
 // LDS address of 16-byte chunk c of row `row` in a swizzled tile is
 // row * 2D + 16 * (c ^ f(row)).  For the MFMA operand reads the lane-dependent part
 // and the loop index separate under XOR: with c = 4*ks + grp (K) or 2*c' + h (V),
@@ -149,7 +183,11 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void pa_prefill_kernel(Prefi
   const int wave_n_hi = min(Qn - 1, (wave_m0 + 16 * kPfBlocks - 1) / G);
   const bool wave_active = wave_m0 < Qn * G;
 
-  // this lane's column in block b: token n_col[b], query head kvh*G + g
+  // this lane's column in block b: token n_col[b], query head kvh*G + g.  With a
+  // negative scale Q is negated here (sign bits: exact, and K.(-q) = -(K.q) exactly)
+  // and |scale| is used, so the scale in the exponent is positive.
+  const float sc = fabsf(a.scale_log2);
+  const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
   int n_col[kPfBlocks];
   bool col_valid[kPfBlocks];
   u32x4 qop[kPfBlocks][KS];
@@ -161,8 +199,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void pa_prefill_kernel(Prefi
     const uint16_t* qrow = a.q + ((size_t)(r0 + n_col[b]) * Hq + kvh * G + m % G) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qop[b][ks] = col_valid[b] ? *reinterpret_cast<const u32x4*>(qrow + 8 * (4 * ks + grp))
-                                : u32x4{0, 0, 0, 0};
+      qop[b][ks] = (col_valid[b] ? *reinterpret_cast<const u32x4*>(qrow + 8 * (4 * ks + grp))
+                                 : u32x4{0, 0, 0, 0}) ^ qsign;
   }
 
   const int bs = a.block_size, mbps = a.max_blocks_per_seq;
@@ -304,11 +342,16 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void pa_prefill_kernel(Prefi
     u32x4 p_hi[kPfBlocks], p_lo[kPfBlocks];
 #pragma unroll
     for (int b = 0; b < kPfBlocks; ++b) {
+      // The scale is folded into the exponent's argument: sc > 0 (a negative scale
+      // has negated Q instead; a zero one arrives as 2^-100), so the column max of
+      // sc * s is sc times the max of the raw scores s, and the probabilities are
+      // 2^(fma(s, sc, -m)).  Keys a step does not keep (past the context, after the
+      // column's token) get s = -inf, hence probability 0.
       float x[2][4];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[h][e] = st[b][h][e] * a.scale_log2;
+        for (int e = 0; e < 4; ++e) x[h][e] = st[b][h][e];
       if (!ctx_step || u0 + kPrefillStep > C) {
         const int lim = ctx_step ? C - 1 : n_col[b];
 #pragma unroll
@@ -317,13 +360,14 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void pa_prefill_kernel(Prefi
           for (int e = 0; e < 4; ++e)
             if (u0 + kTile * h + 4 * grp + e > lim) x[h][e] = kNegInf;
       }
-      float mx = kNegInf;
+      float mr = kNegInf;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, x[h][e]);
-      mx = xor_max<16>(mx);
-      mx = xor_max<32>(mx);
+        for (int e = 0; e < 4; ++e) mr = fmaxf(mr, x[h][e]);
+      mr = xor_max<16>(mr);
+      mr = xor_max<32>(mr);
+      const float mx = mr * sc;
       // The first step a column sees always holds one of its keys (context token 0,
       // or new token 0 when there is no context), so it moves the max to a finite
       // value; later a wave rescales only when one of its columns' max grows by
@@ -337,9 +381,14 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void pa_prefill_kernel(Prefi
         for (int c = 0; c < DB; ++c) acc[b][c] *= alpha;
         l_part[b] *= alpha;
       }
+      float arg[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) arg[h][e] = __builtin_fmaf(x[h][e], sc, -m_run[b]);
       u32x2 ph[2], pl[2];
-      prob_operands<DT>(x[0], m_run[b], ph[0], pl[0]);
-      prob_operands<DT>(x[1], m_run[b], ph[1], pl[1]);
+      prefill_probs<DT>(arg[0], ph[0], pl[0]);
+      prefill_probs<DT>(arg[1], ph[1], pl[1]);
       p_hi[b] = u32x4{ph[0].x, ph[0].y, ph[1].x, ph[1].y};
       p_lo[b] = u32x4{pl[0].x, pl[0].y, pl[1].x, pl[1].y};
       // the exp sum from the same rounded values the PV MFMAs take

@@ -741,7 +741,11 @@ PA_API int paged_attn_prefill(void* out, const void* q, const void* k_new, const
   args.max_query_len = max_query_len;
   args.max_ctx_len = max_ctx_len;
   args.col_blocks = static_cast<int>(col_blocks);
+  // the kernel takes |scale| into the exponent and negates Q for a negative scale; a
+  // zero scale is passed as 2^-100, with which every exponent is below 2^-50 in
+  // magnitude and rounds to weight 1 in fp32, the uniform weights a zero scale means
   args.scale_log2 = scale * kLog2e;
+  if (args.scale_log2 == 0.f) args.scale_log2 = 0x1p-100f;
   const unsigned g = static_cast<unsigned>(grid);
   const bool f16 = dtype == PA_F16;
   switch (head_dim) {

@@ -299,6 +299,8 @@ int paged_attn_decode_ex(void* out, const void* q, const void* key_cache,
  *                       chunks are cut to it); 0 (no new tokens) is a no-op, and the
  *                       row pointers q, k_new, v_new and out may then be NULL
  *   max_ctx_len         host-known bound of ctx_lens, <= max_blocks_per_seq*block_size
+ *   scale               any finite value (a negative one is applied by negating q, which
+ *                       is exact; zero gives every kept key the same weight)
  * Shapes, dtypes and alignment as for decode (k_new and v_new 16-byte aligned).
  * No workspace.  Returns PA_OK or the first error found.
  */

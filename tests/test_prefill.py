@@ -142,3 +142,16 @@ def test_chunked_prefill_workload_sampled():
                 rows.append((r0 + n, h))
     got = np.stack([out[r, h] for r, h in rows])
     assert_close(got, ref(w, rows=rows), "prefill/chunk")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("scale", [0.0, -0.0, -1.0 / 16, -0.7, 1e-6])
+def test_any_finite_scale(scale, dtype):
+    """The kernel folds |scale| into the exponent and negates Q for a negative
+    scale; a zero scale averages the kept keys uniformly.  All against the oracle,
+    with poisoned slots past every context."""
+    say(f"case prefill scale={scale} {dtype}")
+    w = make([0, 1, 15, 16, 17, 100, 333], [1, 7, 16, 17, 40, 3, 65], dtype=dtype, seed=57,
+             scale=scale)
+    assert w.ctx.scale == scale
+    assert_close(gpu_out(run(w)), ref(w), f"prefill/scale{scale}/{dtype}")
