@@ -19,16 +19,20 @@
 // sum, accumulator) in registers.  No barrier and no merge stand between the
 // pieces of a range: a piece that lies inside one range is finished from
 // registers (its output rows), or, for a partial record, parked in a free slot of
-// an LDS pool that the whole workgroup writes out after the walk (stored directly
-// when the pool is full: stores mixed into the saturated read stream cost about
-// ten times their bytes).  Only a piece cut by a range boundary is shared: each
-// later wave holding part of it parks its state in a reserved pool slot (at most
-// one per wave, its first piece), and after the walk the first wave holding it
-// merges the parked parts with the flash-attention rescale and writes the result.
+// an LDS pool that the whole workgroup writes out after the walk, then (head_dim
+// 256) in the wave's spare accumulator registers, written when its walk ends, and
+// stored directly only when both are full: stores mixed into the saturated read
+// stream cost about ten times their bytes.  Only a piece cut by a range boundary
+// is shared: each later wave holding part of it parks its state in a reserved pool
+// slot (at most one per wave, its first piece), and after the walk the first wave
+// holding it merges the parked parts with the flash-attention rescale and writes
+// the result.
 // Records, phase 2 and the job list are those of the other kernels: PARTS uses the
 // fixed-partition record of (sequence, KV head, partition) and the fixed-partition
 // phase 2; the balanced split the two records per workgroup.
 #pragma once
+
+#include <utility>
 
 #include "pa_kernels.h"
 
@@ -36,6 +40,60 @@ namespace pa {
 
 constexpr int kStreamMaxGroup = 16;       // query heads per KV head (the largest group served)
 constexpr float kLazyRescaleLog2 = 8.f;   // slack of the running max before a rescale (base 2)
+
+// Record hold (head_dim 256 with explicit partitions, groups of up to 6 heads): the
+// accumulator registers the kernel leaves free (it allocates 68 of the 256 AGPRs,
+// one wave per SIMD) hold up to kHoldRecs records per wave once the LDS pool is full,
+// so that they too are written after the walk.  A held record is 25 registers per
+// lane: its packed state (24: lane l, register 4i + e holds f32x4 l + 64i of the
+// pool layout, element e), then (max, exp sum) of head h in lanes 2h, 2h+1 and the
+// record index in lanes 2G, 2G+1 (low, high word).  Hold slot k is AGPRs
+// kHoldBase + 25k .. + 24, addressed by number in inline asm: the compiler neither
+// sees nor allocates them (a clobber of a255 at kernel entry makes the kernel
+// allocate the whole AGPR file, and the walk's own accumulators stay in a0 .. a67).
+constexpr int kHoldRecs = 7;
+constexpr int kHoldStride = 25;
+constexpr int kHoldMaxGroup = 6;
+constexpr int kHoldBase = 256 - kHoldRecs * kHoldStride;
+
+template <int R>
+__device__ __forceinline__ void agpr_put(float x) {
+  asm volatile("v_accvgpr_write_b32 a[%1], %0" ::"v"(x), "n"(R));
+}
+template <int R>
+__device__ __forceinline__ float agpr_get() {
+  float x;
+  asm volatile("v_accvgpr_read_b32 %0, a[%1]" : "=v"(x) : "n"(R));
+  return x;
+}
+template <int Base, int... J>
+__device__ __forceinline__ void agpr_put_all(const float (&v)[kHoldStride],
+                                             std::integer_sequence<int, J...>) {
+  (agpr_put<Base + J>(v[J]), ...);
+}
+template <int Base, int... J>
+__device__ __forceinline__ void agpr_get_all(float (&v)[kHoldStride],
+                                             std::integer_sequence<int, J...>) {
+  ((v[J] = agpr_get<Base + J>()), ...);
+}
+template <int K = 0>
+__device__ __forceinline__ void hold_put(int k, const float (&v)[kHoldStride]) {
+  if constexpr (K < kHoldRecs) {
+    if (k == K)
+      agpr_put_all<kHoldBase + K * kHoldStride>(v, std::make_integer_sequence<int, kHoldStride>{});
+    else
+      hold_put<K + 1>(k, v);
+  }
+}
+template <int K = 0>
+__device__ __forceinline__ void hold_get(int k, float (&v)[kHoldStride]) {
+  if constexpr (K < kHoldRecs) {
+    if (k == K)
+      agpr_get_all<kHoldBase + K * kHoldStride>(v, std::make_integer_sequence<int, kHoldStride>{});
+    else
+      hold_get<K + 1>(k, v);
+  }
+}
 
 template <int D, int W>
 struct StreamLdsCore {
@@ -87,6 +145,8 @@ __global__ __launch_bounds__(W * 64, 1) void pa_phase1_stream_kernel(DecodeArgs 
   using Z = Swz<D>;          // K tiles
   using ZV = Swz<D, true>;   // V tiles
   __shared__ __attribute__((aligned(16))) StreamLds<D, W> sm;
+  constexpr bool HOLD = PARTS && D == 256;
+  if constexpr (HOLD) asm volatile("" ::: "a255");   // the kernel allocates every AGPR
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -292,6 +352,43 @@ __global__ __launch_bounds__(W * 64, 1) void pa_phase1_stream_kernel(DecodeArgs 
     if (lane == 0) *reinterpret_cast<long long*>(base + kp4 + 8) = dest;
     return true;
   };
+  // a record finished inside the walk once the pool is full: into the wave's next
+  // hold slot, packed through the wave's tile slot (idle between the tile's last
+  // P.V read and the next tile's staging); false when the slots are used up
+  int n_held = 0;
+  auto hold_piece = [&](long long dest, float M, float Lsum) -> bool {
+    if constexpr (!HOLD) {
+      return false;
+    } else {
+      if (G > kHoldMaxGroup || n_held >= kHoldRecs) return false;
+      f32x4* scratch = reinterpret_cast<f32x4*>(sm.tiles + wave * 2 * TILE_BYTES);
+      float* meta = reinterpret_cast<float*>(scratch + kp4);
+      const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+      wave_lds_fence();
+      if (col < G) {
+#pragma unroll
+        for (int cc = 0; cc < DB; ++cc) scratch[(cc * G + col) * 4 + grp] = acc[cc] * inv;
+        if (grp == 0) {
+          meta[2 * col] = M;
+          meta[2 * col + 1] = Lsum;
+        }
+      }
+      if (lane == 0) *reinterpret_cast<long long*>(meta + 2 * G) = dest;
+      wave_lds_fence();
+      float v[kHoldStride];
+#pragma unroll
+      for (int i = 0; i < kHoldMaxGroup; ++i) {
+        const f32x4 t = scratch[lane + 64 * i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * i + e] = t[e];
+      }
+      v[4 * kHoldMaxGroup] = meta[lane];
+      hold_put(n_held, v);
+      ++n_held;
+      wave_lds_fence();
+      return true;
+    }
+  };
   // a later wave's first piece, begun by an earlier wave: parked for the merge
   auto park = [&](int ps, float M, float Lsum) {
     if (wave == 0) return;       // never: wave 0's pieces all begin inside its run
@@ -472,7 +569,8 @@ __global__ __launch_bounds__(W * 64, 1) void pa_phase1_stream_kernel(DecodeArgs 
         const float Ls = full_sum();
         if (ps >= wa) {
           const long long dest = dest_of(p_s, ps, pe);
-          if (dest < 0 || !pool_piece(dest, m_run, Ls)) write_piece(dest, m_run, Ls);
+          if (dest < 0 || !(pool_piece(dest, m_run, Ls) || hold_piece(dest, m_run, Ls)))
+            write_piece(dest, m_run, Ls);
         } else {
           park(ps, m_run, Ls);
         }
@@ -493,6 +591,29 @@ __global__ __launch_bounds__(W * 64, 1) void pa_phase1_stream_kernel(DecodeArgs 
       else merger = true;
     } else {
       park(ps, m_run, kept_l);
+    }
+  }
+  if constexpr (HOLD) {
+    // the wave's held records, written once its walk is over
+    for (int k = 0; k < n_held; ++k) {
+      float v[kHoldStride];
+      hold_get(k, v);
+      const unsigned lo = static_cast<unsigned>(
+          __builtin_amdgcn_readlane(__float_as_int(v[4 * kHoldMaxGroup]), 2 * G));
+      const unsigned hi = static_cast<unsigned>(
+          __builtin_amdgcn_readlane(__float_as_int(v[4 * kHoldMaxGroup]), 2 * G + 1));
+      const long long d = static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo);
+#pragma unroll
+      for (int i = 0; i < kHoldMaxGroup; ++i) {
+        if (i < G) {
+          const int jj = lane + 64 * i;
+          const int cc = jj / (4 * G), rem = jj - cc * 4 * G;
+          *reinterpret_cast<f32x4*>(a.ws_acc + rec_acc_index(cc, d, rem >> 2, G, a.records) +
+                                    4 * (rem & 3)) =
+              f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+        }
+      }
+      if (lane < 2 * G) reinterpret_cast<float*>(a.ws_ml + d * G)[lane] = v[4 * kHoldMaxGroup];
     }
   }
   // pieces cut by range boundaries: the first wave holding one merges the parked parts
